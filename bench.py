@@ -1,0 +1,219 @@
+"""Benchmark of the shard-local mixed-precision AdamW step on one MI355X.
+
+A step is one pass of the whole hot path over one rank's shard: pass 1
+(unscale, inf/NaN, sum of squares, zero count), the fixed-order reduction,
+the finalize (skip, norm, clip, loss scale, step count) and pass 2 (clip +
+AdamW + bias correction + write-back).  Inputs are synthetic (seeded
+model-shaped param lists) and resident in HBM before the timed region.
+
+Prints one JSON line.  The default workload is a GPT-2-small-shaped param
+list sharded N=8, rank 3, 40M-element buckets, bf16 params and grads.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "shard AdamW step: Gparams/s and achieved HBM GB/s (% of peak), 1 MI355X"
+ES = {"f32": 4, "bf16": 2, "f16": 2}
+
+# HBM traffic of k_apply measured with rocprofv3 PMC counters (FETCH_SIZE,
+# WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
+# reported only while the kernel source is the one that was measured.
+MEASURED_TRAFFIC = {}
+
+
+def _src_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("sharded_mixed_precision_amd/csrc/step.hip", "sharded_mixed_precision_amd/csrc/internal.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pass_bytes(pd: str, gd: str):
+    """Algorithmic HBM bytes per shard element: (pass 1, pass 2).
+
+    Pass 1 reads the grad.  Pass 2 reads grad, master (or the fp32 param),
+    m, v and writes master, m, v and, for 16-bit params, the param."""
+    p1 = ES[gd]
+    p2 = ES[gd] + 12 + 12 + (ES[pd] if pd != "f32" else 0)
+    return p1, p2
+
+
+def cpu_baseline(workload, seconds: float):
+    """The oracle (plain single-threaded C) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    from tests.oracle_harness import OracleRun, to_bits
+
+    params = synth.PARAM_LISTS[workload.model]()
+    O = oracle.Layout(params, workload.dp_size, workload.dp_rank, workload.bucket_size)
+    E = sum(O.buffer(k)["shard_numel"] for k in range(O.num_buffers))
+    hp = [(workload.lr, workload.beta1, workload.beta2, workload.eps, workload.weight_decay)]
+    if E <= (1 << 25):
+        run = OracleRun(params, workload.dp_size, workload.dp_rank, workload.bucket_size)
+        for k, b in enumerate(run.bufs):
+            b["param"][:] = to_bits(synth.fill_normal(b["pd"], b["n"], 0, synth.weight_stream(k), 0, 0.02))
+            b["grad"][:] = to_bits(synth.fill_normal(b["gd"], b["n"], 0, synth.grad_stream(k), 1, workload.grad_sigma))
+        run.init_state()
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            run.step(hp, workload.max_grad_norm)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return {"value": round(E * steps / el / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
+                "sample": f"whole rank window ({E} shard elements), {steps} full oracle steps in {el:.1f}s, "
+                          f"1 thread"}
+    # large windows: the oracle's per-element stats + update on the first
+    # 2^24 arena slots of buffer 0 (same arithmetic per element as a full step)
+    lib = oracle.lib()
+    b0 = O.buffer(0)
+    pd, gd = {0: "f32", 1: "bf16", 2: "f16"}[b0["param_dtype"]], {0: "f32", 1: "bf16", 2: "f16"}[b0["grad_dtype"]]
+    n = min(1 << 24, b0["window_numel"])
+    g = to_bits(synth.fill_normal(gd, n, 0, synth.grad_stream(0), 1, workload.grad_sigma)).copy()
+    p = to_bits(synth.fill_normal(pd, n, 0, synth.weight_stream(0), 0, 0.02)).copy()
+    master = np.zeros(n, np.float32)
+    if pd == "bf16":
+        lib.or_bf16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
+    elif pd == "f16":
+        lib.or_f16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    hg = np.zeros(n, np.int32)
+    sc = oracle.make_scaler(workload.dynamic_scale, workload.initial_scale)
+    t = ctypes.c_int64(0)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        st = oracle.Stats()
+        lib.or_grad_stats_range(O.handle, 0, g.ctypes.data, lib.or_inv_scale(ctypes.byref(sc)), 0, n,
+                                ctypes.byref(st))
+        s = oracle.Scalars()
+        lib.or_decide(ctypes.byref(st), ctypes.byref(sc), ctypes.byref(t), oracle.make_hparams(hp), 1,
+                      workload.max_grad_norm, ctypes.byref(s))
+        lib.or_apply_elems(oracle.DTYPES[pd], oracle.DTYPES[gd], n, hg.ctypes.data, g.ctypes.data,
+                           master.ctypes.data, m.ctypes.data, v.ctypes.data, p.ctypes.data, ctypes.byref(s))
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(n * steps / el / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} arena slots of buffer 0 of the rank window, {steps} oracle stats+update "
+                      f"passes in {el:.1f}s, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2-small")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the step; runs on more than one GPU are not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sharded_mixed_precision_amd as D
+    from sharded_mixed_precision_amd.arena import DeviceArenas
+
+    w = synth.WORKLOADS[args.workload]
+    params = synth.PARAM_LISTS[w.model]()
+    L = D.dopt_build_ranges(params, w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
+    A = DeviceArenas(L)
+    stream = torch.cuda.current_stream()
+    E = 0
+    bytes_step = 0
+    apply_bytes = 0
+    for k, info in enumerate(A.info):
+        p1, p2 = pass_bytes(info["pd"], info["gd"])
+        E += info["shard_numel"]
+        bytes_step += (p1 + p2) * info["shard_numel"]
+        apply_bytes += p2 * info["shard_numel"]
+        A.bufs[k]["param"].copy_(synth.fill_normal(info["pd"], info["n"], w.seed, synth.weight_stream(k), 0,
+                                                   w.weight_sigma))
+        A.bufs[k]["grad"].copy_(synth.fill_normal(info["gd"], info["n"], w.seed, synth.grad_stream(k), 1,
+                                                  w.grad_sigma, scale=w.initial_scale, zero_frac=w.zero_frac))
+    D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
+    bufs_c = D.tensors(A.bufs)
+    hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
+
+    def step(ev_a=None, ev_b=None):
+        D.dopt_step_stats(L, bufs_c, A.workspace, stream)
+        D.dopt_step_finalize(L, hp_c, w.max_grad_norm, A.workspace, stream)
+        if ev_a is not None:
+            ev_a.record(stream)
+        D.dopt_step_apply(L, bufs_c, A.workspace, stream)
+        if ev_b is not None:
+            ev_b.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(ev_a[i], ev_b[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    apply_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / K
+    st = D.dopt_read_stats(L, A.workspace, stream)
+    assert st["skipped"] == 0 and st["step_count"] == args.warmup + K, st
+    ms = total_ms / K
+    value = E / (ms * 1e-3) / 1e9
+    gbps = bytes_step / (ms * 1e-3) / 1e9
+    ach = apply_bytes / (apply_ms * 1e-3) / 1e9
+    tr = MEASURED_TRAFFIC.get(args.workload)
+    traffic = tr["bytes_per_launch"] if tr and tr.get("src") == _src_sha() else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {len(params)}-param list, rank {w.dp_rank} of N={w.dp_size}, "
+                               f"bucket {w.bucket_size}, {E} shard elements",
+                   "shard_elements": E, "bytes_per_step": bytes_step},
+        "hbm_GBps_step": round(gbps, 1),
+        "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "launch_ms": round(apply_ms, 5),
+                     "algorithmic_bytes_per_launch": apply_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

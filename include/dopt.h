@@ -1,0 +1,292 @@
+/*
+ * dopt.h -- C ABI of the shard-local mixed-precision AdamW step of a ZeRO-1
+ * distributed optimizer, for AMD Instinct MI355X (gfx950).
+ *
+ * One data-parallel rank owns a contiguous 1/N slice ("window") of every
+ * bucket of every flat grad buffer; the slice cuts across parameter
+ * boundaries.  Per step the library unscales the rank's grads into fp32,
+ * detects inf/NaN, takes the L2 norm and the clip coefficient, updates the
+ * fp32 master weights and Adam moments (AdamW with bias correction), and
+ * writes the 16-bit params back into the rank's param window.  The
+ * reduce-scatter before the step and the all-gather after it are the
+ * caller's.
+ *
+ * Pages cited (title, then section):
+ *   [DO] "Megatron-LM distrib_optimizer.py 源码精读"
+ *   [ZL] "02 · ZeRO 显存账本与 Megatron DistributedOptimizer"
+ *   [DP] "Megatron-LM distributed 包深度解析：DDP 梯度同步与 finalize_model_grads 全流程"
+ *   [DS] "Megatron-LM与DeepSpeed的分布式训练源码里，模型和优化器到底是怎么切分的？"
+ *
+ * Conventions
+ *   - Every function returns 0 on success or a negative DOPT_ERR_* code;
+ *     dopt_last_error() then holds a message (per thread).  No exception or
+ *     abort crosses the ABI.
+ *   - "host" pointers are CPU memory, "device" pointers are GPU memory
+ *     (e.g. from hipMalloc or a PyTorch CUDA tensor).  The library never
+ *     allocates or frees device memory.
+ *   - Device work is enqueued on the caller's HIP stream and is ordered with
+ *     the caller's other work on that stream; nothing synchronizes unless a
+ *     function says so.
+ *   - A dopt_layout is immutable once built and may be shared by threads.
+ *     Calls that use one workspace must not overlap in time.
+ */
+#ifndef DOPT_H
+#define DOPT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- element types ---- */
+enum { DOPT_F32 = 0, DOPT_BF16 = 1, DOPT_F16 = 2 };
+
+/* ---- error codes ---- */
+enum {
+    DOPT_OK = 0,
+    DOPT_ERR_INVALID = -1, /* bad argument (null, out of range, bad dtype, misaligned pointer) */
+    DOPT_ERR_ASSERT = -2,  /* a layout invariant of [DO] "最终内存大小断言" does not hold */
+    DOPT_ERR_NOMEM = -3,   /* host allocation failed */
+    DOPT_ERR_HIP = -4,     /* a HIP runtime call failed (message names it) */
+    DOPT_ERR_RANGE = -5    /* query index out of range */
+};
+
+/* ---- group kinds of [DO] "五组数据结构 / 分片切片逻辑" and [ZL] §3 ---- */
+enum {
+    DOPT_GROUP_MODEL_FLOAT16 = 0,
+    DOPT_GROUP_MODEL_FP32 = 1,
+    DOPT_GROUP_SHARD_FLOAT16 = 2,
+    DOPT_GROUP_SHARD_FP32_FROM_FLOAT16 = 3,
+    DOPT_GROUP_SHARD_FP32 = 4
+};
+
+enum { DOPT_SCALER_CONSTANT = 0, DOPT_SCALER_DYNAMIC = 1 };
+
+#define DOPT_MAX_HGROUPS 16
+/* Arena arrays hold a whole number of DOPT_ARENA_ALIGN elements. */
+#define DOPT_ARENA_ALIGN 2048
+/* Required alignment (bytes) of every device pointer passed in. */
+#define DOPT_PTR_ALIGN 256
+
+/* One model parameter, in model (registration, forward) order. */
+typedef struct dopt_param_desc {
+    int64_t numel;               /* > 0 */
+    int32_t param_dtype;         /* DOPT_F32 / DOPT_BF16 / DOPT_F16 */
+    int32_t grad_dtype;          /* the grad buffer's element type */
+    int32_t requires_new_bucket; /* nonzero: the param gets a bucket of its own */
+    int32_t hgroup;              /* optimizer param group, 0 <= hgroup < DOPT_MAX_HGROUPS */
+} dopt_param_desc;
+
+typedef struct dopt_shard_cfg {
+    int32_t dp_size;             /* N >= 1 */
+    int32_t dp_rank;             /* 0 <= r < N */
+    int64_t bucket_size;         /* elements; <= 0: no size trigger (one bucket) */
+    int32_t pad_for_high_busbw;  /* nonzero: buckets padded to lcm(N,128,2^16) */
+    int32_t reserved;            /* 0 */
+} dopt_shard_cfg;
+
+typedef struct dopt_range { int64_t start, end; } dopt_range;
+
+typedef struct dopt_layout dopt_layout;
+
+/*
+ * dopt_build_ranges -- the host-side shard-range mapper.
+ *
+ * Groups the params into one flat buffer per (param dtype, grad dtype) in
+ * order of first appearance ([DP] §2.2 (3)); lays each buffer out last param
+ * first, starting every param on a multiple of 64 elements and closing a
+ * bucket when it reaches bucket_size or for a param that needs its own
+ * bucket ([DO] "Bucket 划分算法：逆序遍历 + 尺寸触发"); pads every bucket end to
+ * a multiple of lcm(N, 128) (or lcm(N, 128, 2^16)) ([DO] "两级 Padding 机制");
+ * checks the size invariants ([DO] "最终内存大小断言"); takes rank r's
+ * window of every bucket ([DO] "Bucket 级别的均等切分"); intersects every
+ * param with its bucket's window in the four coordinate views of [DO]
+ * "Range 类：四种视角的统一抽象"; and forms the shard groups ([DO] group
+ * building section; [ZL] §3).
+ *
+ * It also fixes the device layout the step uses: per buffer, an "arena" of
+ * arena_numel elements holding the rank's windows of that buffer's buckets
+ * back to back in bucket order (bucket b's window at arena_offset of b).
+ * The grad window, the param window, the fp32 master and both Adam moments
+ * of a buffer are all arrays in this one index space.
+ *
+ * params: host, n entries, model order; cfg: host.  *out receives a layout
+ * owned by the library; free it with dopt_layout_free.
+ * Errors: DOPT_ERR_INVALID (null pointers, n <= 0, numel <= 0, bad dtype or
+ * hgroup, N < 1, r outside [0, N)); DOPT_ERR_ASSERT; DOPT_ERR_NOMEM.
+ */
+int dopt_build_ranges(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg,
+                      dopt_layout **out);
+
+void dopt_layout_free(dopt_layout *layout);
+
+/* ---- read-only layout queries (host; no device work) ---- */
+
+typedef struct dopt_buffer_info {
+    int32_t param_dtype, grad_dtype;
+    int32_t n_buckets;
+    int32_t n_params;
+    int64_t numel;          /* padded buffer size ([DO] "最终内存大小断言") */
+    int64_t numel_unpadded; /* sum of per-bucket unpadded sizes */
+    int64_t window_numel;   /* sum of the rank's window sizes */
+    int64_t arena_numel;    /* window_numel rounded up to DOPT_ARENA_ALIGN: size of every arena array */
+    int64_t shard_numel;    /* param elements inside the rank's windows */
+} dopt_buffer_info;
+
+typedef struct dopt_bucket_info {
+    int64_t offset;         /* bucket start in the buffer */
+    int64_t numel;          /* padded bucket size, a multiple of N */
+    int64_t numel_unpadded;
+    int64_t shard_size;     /* numel / N */
+    int64_t window_start;   /* offset + r * shard_size (buffer coordinates) */
+    int64_t arena_offset;   /* where the window starts in the arena */
+    int32_t n_params;
+    int32_t reserved;
+} dopt_bucket_info;
+
+/* Four views of one param's shard on this rank ([DO] "Range 类"). */
+typedef struct dopt_param_info {
+    int32_t buffer, bucket;
+    int32_t has_shard;          /* 0: no element of the param is in this rank's window */
+    int32_t hgroup;
+    int64_t start, end;         /* the param's range in its buffer (param_index_map) */
+    dopt_range gbuf_world;      /* shard, buffer coordinates */
+    dopt_range gbuf_world_in_bucket; /* shard, bucket coordinates */
+    dopt_range gbuf_local;      /* shard, window coordinates */
+    dopt_range param;           /* shard, coordinates inside the param */
+    int64_t arena_offset;       /* shard start in the arena; -1 without a shard */
+} dopt_param_info;
+
+int32_t dopt_layout_num_buffers(const dopt_layout *layout);
+int dopt_layout_buffer(const dopt_layout *layout, int32_t k, dopt_buffer_info *out);
+int dopt_layout_bucket(const dopt_layout *layout, int32_t k, int32_t b, dopt_bucket_info *out);
+/* Window of rank `rank` (any rank, not only this one) in bucket b of buffer k,
+ * buffer coordinates ([DO] "Bucket 级别的均等切分": all ranks' ranges). */
+int dopt_layout_rank_window(const dopt_layout *layout, int32_t k, int32_t b, int32_t rank, dopt_range *out);
+int dopt_layout_param(const dopt_layout *layout, int64_t p, dopt_param_info *out);
+/* Model-order indices of the params of one group kind and hyper-group; writes
+ * at most cap entries to idx (host, may be NULL) and returns the full count,
+ * or a negative error code. */
+int64_t dopt_layout_group(const dopt_layout *layout, int32_t kind, int32_t hgroup, int64_t *idx, int64_t cap);
+/* Param elements on this rank over all buffers (the optimizer-state length
+ * of the ledger in [ZL] §2). */
+int64_t dopt_layout_state_numel(const dopt_layout *layout);
+
+/* Bytes of device workspace the step needs.  The caller allocates it
+ * (DOPT_PTR_ALIGN-aligned), passes it to dopt_init_state and then to every
+ * step, and keeps it alive: it carries the step count and the loss-scale
+ * state from step to step. */
+int64_t dopt_workspace_bytes(const dopt_layout *layout);
+
+/* ---- device arrays of one flat buffer (all in arena coordinates) ---- */
+typedef struct dopt_buffer_tensors {
+    const void *grad;   /* device, arena_numel x grad dtype: the rank's reduced grads; read only */
+    void *param;        /* device, arena_numel x param dtype: the rank's param windows; written back */
+    float *master;      /* device, arena_numel fp32; NULL when the param dtype is fp32 */
+    float *exp_avg;     /* device, arena_numel fp32: Adam m */
+    float *exp_avg_sq;  /* device, arena_numel fp32: Adam v */
+} dopt_buffer_tensors;
+
+typedef struct dopt_scaler_cfg {
+    int32_t kind;            /* DOPT_SCALER_CONSTANT or DOPT_SCALER_DYNAMIC */
+    int32_t hysteresis;      /* dynamic: overflows tolerated before a backoff (>= 1) */
+    int64_t growth_interval; /* dynamic: clean steps between growths (>= 1) */
+    double initial_scale;    /* > 0 */
+    double growth_factor;    /* dynamic, > 1 */
+    double backoff_factor;   /* dynamic, in (0, 1) */
+    double min_scale;        /* dynamic, > 0 */
+} dopt_scaler_cfg;
+
+/*
+ * dopt_init_state -- S1 of the step: fp32 master = upcast of the 16-bit
+ * param window ([DO] "分片切片逻辑": clone of the shard, as float), Adam
+ * moments = 0; fp32-param buffers get no master ([ZL] §3).  Loads the tile
+ * tables into the workspace and sets step count 0 and the loss scale to
+ * scaler->initial_scale.
+ *
+ * bufs: host array of dopt_layout_num_buffers() entries holding device
+ * pointers; scaler: host; workspace: device, dopt_workspace_bytes() bytes.
+ * Synchronizes `stream` before returning (the tables are copied from the
+ * layout's host memory).
+ * Errors: DOPT_ERR_INVALID (null / misaligned pointers, bad scaler),
+ * DOPT_ERR_HIP.
+ */
+int dopt_init_state(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const dopt_scaler_cfg *scaler,
+                    void *workspace, hipStream_t stream);
+
+/* Hyper-parameters of one optimizer param group (AdamW). */
+typedef struct dopt_hparams {
+    double lr, beta1, beta2, eps, weight_decay;
+} dopt_hparams;
+
+/* Result of one step (host copy of the device record). */
+typedef struct dopt_stats {
+    int32_t found_inf;      /* 1: some unscaled grad was inf or NaN */
+    int32_t skipped;        /* 1: no state was changed this step */
+    int32_t clip_applied;   /* 1: grads were scaled by clip_coef */
+    int32_t reserved;
+    double sumsq;           /* sum of squares of the unscaled, pre-clip grads */
+    double grad_norm;       /* sqrt(sumsq) */
+    double clip_coef;       /* max_grad_norm / (grad_norm + 1e-6); 1.0 when not clipping */
+    uint64_t num_zeros;     /* unscaled grad elements equal to zero */
+    double loss_scale_used; /* scale the grads of this step carried */
+    double loss_scale_next; /* scale for the next step */
+    int64_t step_count;     /* successful steps so far (Adam's t) */
+} dopt_stats;
+
+/*
+ * dopt_step -- one optimizer step on this rank's shard, in the order of
+ * [DO] "三层继承体系" (second layer): grads to fp32 + unscale + inf/NaN check,
+ * clip by the global norm, then the inner AdamW step and the copy of the
+ * masters back to the 16-bit params ([DO] "分片切片逻辑"; [DS] §2 step).
+ * Equivalent to dopt_step_stats, dopt_step_finalize and dopt_step_apply in
+ * that order.  A step with an inf/NaN grad is skipped: master, moments,
+ * params and the step count stay as they were, and a dynamic loss scale
+ * backs off.  Skipping is not an error.
+ *
+ * bufs: host array (device pointers); hp: host, n_hgroups entries (one per
+ * hyper-group used by the params); max_grad_norm <= 0 disables clipping.
+ * out: host, may be NULL; when given, the call synchronizes `stream` and
+ * fills it.  Errors: DOPT_ERR_INVALID, DOPT_ERR_HIP.
+ */
+int dopt_step(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const dopt_hparams *hp,
+              int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream, dopt_stats *out);
+
+/*
+ * The step in three parts.  Between dopt_step_stats and dopt_step_finalize a
+ * multi-rank caller sums the grad-stats record (dopt_stats_record) over the
+ * whole distributed-optimizer group, on the same stream: [DO] "三层继承体系"
+ * (third layer) takes the grad norm over all data-parallel ranks.  On one
+ * rank no exchange is needed.
+ *
+ * dopt_step_stats: pass 1 -- unscale, sum of squares and zero count over the
+ *   rank's shard elements, reduced in a fixed order into the record.
+ * dopt_step_finalize: skip decision (record not finite), norm, clip
+ *   coefficient, loss-scale update, step count, per-group AdamW scalars.
+ * dopt_step_apply: pass 2 -- clip + AdamW + bias correction + write-back;
+ *   returns immediately on the device when the step is skipped.
+ */
+int dopt_step_stats(const dopt_layout *layout, const dopt_buffer_tensors *bufs, void *workspace,
+                    hipStream_t stream);
+int dopt_step_finalize(const dopt_layout *layout, const dopt_hparams *hp, int32_t n_hgroups, double max_grad_norm,
+                       void *workspace, hipStream_t stream);
+int dopt_step_apply(const dopt_layout *layout, const dopt_buffer_tensors *bufs, void *workspace,
+                    hipStream_t stream);
+
+/* Byte offset in the workspace of the grad-stats record: two doubles,
+ * {sum of squares, zero count}; both are sums over ranks.  A non-finite sum
+ * of squares means some rank found an inf/NaN. */
+int64_t dopt_stats_record_offset(const dopt_layout *layout);
+
+/* Copy the last step's stats to `out` (host); synchronizes `stream`. */
+int dopt_read_stats(const dopt_layout *layout, const void *workspace, hipStream_t stream, dopt_stats *out);
+
+/* Message for the last failing call on this thread (static storage). */
+const char *dopt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

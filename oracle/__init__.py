@@ -102,6 +102,7 @@ def _load():
         "or_f16_to_f32_n": ([VP, VP, I64], None),
         "or_init_state": ([VP, P(Arrays)], None),
         "or_grad_stats": ([VP, P(Arrays), ctypes.c_float, P(Stats)], None),
+        "or_grad_stats_range": ([VP, I32, VP, ctypes.c_float, I64, I64, P(Stats)], None),
         "or_decide": ([P(Stats), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Scalars)], ctypes.c_int),
         "or_apply": ([VP, P(Arrays), P(Scalars)], None),
         "or_apply_elems": ([I32, I32, I64, VP, VP, VP, VP, VP, VP, P(Scalars)], None),

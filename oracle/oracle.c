@@ -455,6 +455,35 @@ float or_inv_scale(const or_scaler *sc) { return (float)(1.0 / sc->scale); }
  *   sumsq = sum of g*g, each square and the running sum in double
  *   zeros = count of g == 0
  */
+/*
+ * S2 restricted to arena slots [lo, hi) of buffer k: the same per-element
+ * work as or_grad_stats, returned as a partial (sumsq, zeros, found_inf) so a
+ * caller can split one large pass into disjoint ranges and add the partials.
+ */
+void or_grad_stats_range(const or_layout *L, int32_t k, const void *grad, float inv_scale, int64_t lo, int64_t hi,
+                         or_stats *st) {
+    f16_table_init();
+    double sumsq = 0.0;
+    uint64_t zeros = 0;
+    int32_t found_inf = 0;
+    const ob_buffer *B = &L->buf[k];
+    for (int64_t s = 0; s < B->n_segs; ++s) {
+        int64_t a = B->seg_start[s], e = B->seg_start[s] + B->seg_len[s];
+        if (a < lo) a = lo;
+        if (e > hi) e = hi;
+        for (int64_t i = a; i < e; ++i) {
+            float g = load_f32(grad, B->gd, i) * inv_scale;
+            if (!isfinite(g)) found_inf = 1;
+            double gd = (double)g;
+            sumsq += gd * gd;
+            if (g == 0.0f) zeros++;
+        }
+    }
+    st->sumsq = sumsq;
+    st->zeros = zeros;
+    st->found_inf = found_inf;
+}
+
 void or_grad_stats(const or_layout *L, const or_arrays *bufs, float inv_scale, or_stats *st) {
     f16_table_init();
     double sumsq = 0.0;

@@ -127,6 +127,9 @@ typedef struct {
 void or_init_state(const or_layout *L, or_arrays *bufs);
 /* S2: unscale, inf/NaN, sum of squares, zeros over the rank's shard elements. */
 void or_grad_stats(const or_layout *L, const or_arrays *bufs, float inv_scale, or_stats *st);
+/* S2 over arena slots [lo, hi) of buffer k only (a partial of the above). */
+void or_grad_stats_range(const or_layout *L, int32_t k, const void *grad, float inv_scale, int64_t lo, int64_t hi,
+                         or_stats *st);
 /* S3: skip decision, norm, clip, loss-scale update, step count, scalars. */
 int or_decide(or_stats *st, or_scaler *sc, int64_t *t, const or_hparams *hp, int32_t nh,
               double max_norm, or_scalars *out);

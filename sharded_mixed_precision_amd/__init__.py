@@ -1,0 +1,314 @@
+"""Python binding of libdopt.so, the shard-local mixed-precision AdamW step
+of a ZeRO-1 distributed optimizer for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every computation happens in the library (host
+range mapper in C++, the step in HIP kernels).  Function names match the C
+ABI in include/dopt.h.  Device buffers may be given as PyTorch CUDA tensors
+or raw integer addresses; PyTorch is used only to own device memory and
+streams.  There is no fallback: if the library is not built, import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdopt.so")
+
+DOPT_F32, DOPT_BF16, DOPT_F16 = 0, 1, 2
+DTYPES = {"f32": DOPT_F32, "bf16": DOPT_BF16, "f16": DOPT_F16}
+DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
+DOPT_SCALER_CONSTANT, DOPT_SCALER_DYNAMIC = 0, 1
+GROUP_KINDS = {"model_float16": 0, "model_fp32": 1, "shard_float16": 2, "shard_fp32_from_float16": 3,
+               "shard_fp32": 4}
+DOPT_MAX_HGROUPS = 16
+DOPT_ARENA_ALIGN = 2048
+DOPT_PTR_ALIGN = 256
+
+
+class DoptError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dopt error {code}: {msg}")
+        self.code = code
+
+
+class dopt_param_desc(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("requires_new_bucket", ctypes.c_int32), ("hgroup", ctypes.c_int32)]
+
+
+class dopt_shard_cfg(ctypes.Structure):
+    _fields_ = [("dp_size", ctypes.c_int32), ("dp_rank", ctypes.c_int32), ("bucket_size", ctypes.c_int64),
+                ("pad_for_high_busbw", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class dopt_range(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("end", ctypes.c_int64)]
+
+    def tuple(self):
+        return (self.start, self.end)
+
+
+class dopt_buffer_info(ctypes.Structure):
+    _fields_ = [("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
+                ("n_params", ctypes.c_int32), ("numel", ctypes.c_int64), ("numel_unpadded", ctypes.c_int64),
+                ("window_numel", ctypes.c_int64), ("arena_numel", ctypes.c_int64), ("shard_numel", ctypes.c_int64)]
+
+
+class dopt_bucket_info(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("numel", ctypes.c_int64), ("numel_unpadded", ctypes.c_int64),
+                ("shard_size", ctypes.c_int64), ("window_start", ctypes.c_int64), ("arena_offset", ctypes.c_int64),
+                ("n_params", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class dopt_param_info(ctypes.Structure):
+    _fields_ = [("buffer", ctypes.c_int32), ("bucket", ctypes.c_int32), ("has_shard", ctypes.c_int32),
+                ("hgroup", ctypes.c_int32), ("start", ctypes.c_int64), ("end", ctypes.c_int64),
+                ("gbuf_world", dopt_range), ("gbuf_world_in_bucket", dopt_range), ("gbuf_local", dopt_range),
+                ("param", dopt_range), ("arena_offset", ctypes.c_int64)]
+
+
+class dopt_buffer_tensors(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("param", ctypes.c_void_p), ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p)]
+
+
+class dopt_scaler_cfg(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("hysteresis", ctypes.c_int32), ("growth_interval", ctypes.c_int64),
+                ("initial_scale", ctypes.c_double), ("growth_factor", ctypes.c_double),
+                ("backoff_factor", ctypes.c_double), ("min_scale", ctypes.c_double)]
+
+
+class dopt_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class dopt_stats(ctypes.Structure):
+    _fields_ = [("found_inf", ctypes.c_int32), ("skipped", ctypes.c_int32), ("clip_applied", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("sumsq", ctypes.c_double), ("grad_norm", ctypes.c_double),
+                ("clip_coef", ctypes.c_double), ("num_zeros", ctypes.c_uint64), ("loss_scale_used", ctypes.c_double),
+                ("loss_scale_next", ctypes.c_double), ("step_count", ctypes.c_int64)]
+
+    def as_dict(self) -> Dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python sharded_mixed_precision_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, VP, D = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+    sig = {
+        "dopt_build_ranges": ([P(dopt_param_desc), I64, P(dopt_shard_cfg), P(VP)], ctypes.c_int),
+        "dopt_layout_free": ([VP], None),
+        "dopt_layout_num_buffers": ([VP], I32),
+        "dopt_layout_buffer": ([VP, I32, P(dopt_buffer_info)], ctypes.c_int),
+        "dopt_layout_bucket": ([VP, I32, I32, P(dopt_bucket_info)], ctypes.c_int),
+        "dopt_layout_rank_window": ([VP, I32, I32, I32, P(dopt_range)], ctypes.c_int),
+        "dopt_layout_param": ([VP, I64, P(dopt_param_info)], ctypes.c_int),
+        "dopt_layout_group": ([VP, I32, I32, VP, I64], I64),
+        "dopt_layout_state_numel": ([VP], I64),
+        "dopt_workspace_bytes": ([VP], I64),
+        "dopt_init_state": ([VP, P(dopt_buffer_tensors), P(dopt_scaler_cfg), VP, VP], ctypes.c_int),
+        "dopt_step": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP, P(dopt_stats)], ctypes.c_int),
+        "dopt_step_stats": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
+        "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
+        "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
+        "dopt_stats_record_offset": ([VP], I64),
+        "dopt_read_stats": ([VP, VP, VP, P(dopt_stats)], ctypes.c_int),
+        "dopt_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+_lib = _load()
+EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", "dopt_layout_buffer",
+            "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
+            "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_stats",
+            "dopt_step_finalize", "dopt_step_apply", "dopt_stats_record_offset", "dopt_read_stats",
+            "dopt_last_error")
+
+
+def lib():
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DoptError(rc, _lib.dopt_last_error().decode())
+
+
+def _addr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+class Layout:
+    """Owns a dopt_layout handle (freed with the object)."""
+
+    def __init__(self, handle: ctypes.c_void_p, dp_size: int, dp_rank: int, n_params: int):
+        self._h = handle
+        self.dp_size, self.dp_rank, self.n_params = dp_size, dp_rank, n_params
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None:
+            _lib.dopt_layout_free(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def num_buffers(self) -> int:
+        return int(_lib.dopt_layout_num_buffers(self._h))
+
+    def buffer(self, k: int) -> Dict:
+        o = dopt_buffer_info()
+        _check(_lib.dopt_layout_buffer(self._h, k, ctypes.byref(o)))
+        return {name: getattr(o, name) for name, _ in o._fields_}
+
+    def bucket(self, k: int, b: int) -> Dict:
+        o = dopt_bucket_info()
+        _check(_lib.dopt_layout_bucket(self._h, k, b, ctypes.byref(o)))
+        return {name: getattr(o, name) for name, _ in o._fields_ if name != "reserved"}
+
+    def rank_window(self, k: int, b: int, rank: int):
+        o = dopt_range()
+        _check(_lib.dopt_layout_rank_window(self._h, k, b, rank, ctypes.byref(o)))
+        return o.tuple()
+
+    def param(self, p: int) -> Dict:
+        o = dopt_param_info()
+        _check(_lib.dopt_layout_param(self._h, p, ctypes.byref(o)))
+        d = {name: getattr(o, name) for name, _ in o._fields_}
+        for key in ("gbuf_world", "gbuf_world_in_bucket", "gbuf_local", "param"):
+            d[key] = d[key].tuple()
+        return d
+
+    def group(self, kind: str, hgroup: int = 0) -> List[int]:
+        k = GROUP_KINDS[kind]
+        n = _lib.dopt_layout_group(self._h, k, hgroup, None, 0)
+        if n < 0:
+            _check(int(n))
+        arr = (ctypes.c_int64 * max(n, 1))()
+        _lib.dopt_layout_group(self._h, k, hgroup, arr, n)
+        return list(arr[:n])
+
+    @property
+    def state_numel(self) -> int:
+        return int(_lib.dopt_layout_state_numel(self._h))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(_lib.dopt_workspace_bytes(self._h))
+
+    @property
+    def stats_record_offset(self) -> int:
+        return int(_lib.dopt_stats_record_offset(self._h))
+
+
+def dopt_build_ranges(params: Sequence, dp_size: int, dp_rank: int, bucket_size: int = 0,
+                      pad_for_high_busbw: int = 0) -> Layout:
+    """params: objects with numel, param_dtype, grad_dtype ('f32'|'bf16'|'f16'),
+    optional requires_new_bucket and hgroup, in model order."""
+    n = len(params)
+    arr = (dopt_param_desc * n)()
+    for i, p in enumerate(params):
+        arr[i].numel = p.numel
+        arr[i].param_dtype = DTYPES[p.param_dtype] if isinstance(p.param_dtype, str) else p.param_dtype
+        arr[i].grad_dtype = DTYPES[p.grad_dtype] if isinstance(p.grad_dtype, str) else p.grad_dtype
+        arr[i].requires_new_bucket = int(getattr(p, "requires_new_bucket", 0))
+        arr[i].hgroup = int(getattr(p, "hgroup", 0))
+    cfg = dopt_shard_cfg(dp_size, dp_rank, bucket_size, pad_for_high_busbw, 0)
+    h = ctypes.c_void_p()
+    _check(_lib.dopt_build_ranges(arr, n, ctypes.byref(cfg), ctypes.byref(h)))
+    return Layout(h, dp_size, dp_rank, n)
+
+
+def _tensors(bufs: Sequence[Dict]) -> ctypes.Array:
+    arr = (dopt_buffer_tensors * len(bufs))()
+    for k, b in enumerate(bufs):
+        arr[k].grad = _addr(b.get("grad"))
+        arr[k].param = _addr(b.get("param"))
+        arr[k].master = _addr(b.get("master"))
+        arr[k].exp_avg = _addr(b.get("exp_avg"))
+        arr[k].exp_avg_sq = _addr(b.get("exp_avg_sq"))
+    return arr
+
+
+def scaler_cfg(dynamic: bool = False, initial_scale: float = 1.0, growth_factor: float = 2.0,
+               backoff_factor: float = 0.5, growth_interval: int = 1000, hysteresis: int = 1,
+               min_scale: float = 1.0) -> dopt_scaler_cfg:
+    return dopt_scaler_cfg(DOPT_SCALER_DYNAMIC if dynamic else DOPT_SCALER_CONSTANT, hysteresis, growth_interval,
+                           initial_scale, growth_factor, backoff_factor, min_scale)
+
+
+def _hparams(hps: Sequence) -> ctypes.Array:
+    arr = (dopt_hparams * len(hps))()
+    for i, h in enumerate(hps):
+        arr[i] = dopt_hparams(*h) if not isinstance(h, dopt_hparams) else h
+    return arr
+
+
+def dopt_init_state(layout: Layout, bufs: Sequence[Dict], scaler: dopt_scaler_cfg, workspace, stream=None):
+    _check(_lib.dopt_init_state(layout.handle, _tensors(bufs), ctypes.byref(scaler), _addr(workspace),
+                                _stream(stream)))
+
+
+def dopt_step(layout: Layout, bufs, hparams: Sequence, max_grad_norm: float, workspace, stream=None,
+              want_stats: bool = True, _tensors_cache=None):
+    st = dopt_stats() if want_stats else None
+    t = _tensors_cache if _tensors_cache is not None else _tensors(bufs)
+    hp = _hparams(hparams)
+    _check(_lib.dopt_step(layout.handle, t, hp, len(hparams), max_grad_norm, _addr(workspace), _stream(stream),
+                          ctypes.byref(st) if st is not None else None))
+    return st.as_dict() if st is not None else None
+
+
+def dopt_step_stats(layout: Layout, bufs, workspace, stream=None):
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    _check(_lib.dopt_step_stats(layout.handle, t, _addr(workspace), _stream(stream)))
+
+
+def dopt_step_finalize(layout: Layout, hparams, max_grad_norm: float, workspace, stream=None):
+    hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
+    _check(_lib.dopt_step_finalize(layout.handle, hp, len(hp), max_grad_norm, _addr(workspace), _stream(stream)))
+
+
+def dopt_step_apply(layout: Layout, bufs, workspace, stream=None):
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    _check(_lib.dopt_step_apply(layout.handle, t, _addr(workspace), _stream(stream)))
+
+
+def dopt_read_stats(layout: Layout, workspace, stream=None) -> Dict:
+    st = dopt_stats()
+    _check(_lib.dopt_read_stats(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
+    return st.as_dict()
+
+
+def dopt_last_error() -> str:
+    return _lib.dopt_last_error().decode()
+
+
+tensors = _tensors
+hparams_array = _hparams

@@ -1,0 +1,87 @@
+// Internal layout structures shared by the host mapper (mapper.cpp) and the
+// step driver / kernels (step.hip).  Not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "dopt.h"
+
+namespace dopt {
+
+// Work unit of the device passes: one tile = TILE consecutive arena elements,
+// handled by one 256-thread workgroup, 8 consecutive elements per thread.
+constexpr int kBlock = 256;
+constexpr int kVec = 8;
+constexpr int kTile = kBlock * kVec;
+static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile size");
+
+// Workgroups per launch (grid-stride over tiles).  Fixed per layout so that
+// the reduction order, and hence the sum of squares, does not depend on the
+// device it runs on.
+constexpr int kStatsMaxBlocks = 1024;
+constexpr int kApplyMaxBlocks = 2048;
+
+// Tile descriptor: the param segments that overlap the tile.
+constexpr int32_t kTileFull = 1 << 30;   // the tile lies inside one segment
+constexpr int32_t kTileCountMask = kTileFull - 1;
+struct TileDesc {
+    int32_t seg_first;
+    int32_t seg_count;  // number of overlapping segments | kTileFull
+};
+
+// A param's shard in arena coordinates, [start, end).
+struct SegDesc {
+    int64_t start, end;
+    int32_t hgroup, pad;
+};
+
+struct Bucket {
+    int64_t offset = 0, numel = 0, unpadded = 0, shard = 0, window_start = 0, arena_offset = 0;
+    int32_t n_params = 0;
+};
+
+struct Param {
+    int64_t numel = 0;
+    int32_t pd = 0, gd = 0, newb = 0, hgroup = 0;
+    int32_t buffer = 0, bucket = 0;
+    int64_t start = 0, end = 0;
+    int32_t has_shard = 0;
+    dopt_range world{0, 0}, world_in_bucket{0, 0}, local{0, 0}, prange{0, 0};
+    int64_t arena = -1;
+};
+
+struct Buffer {
+    int32_t pd = 0, gd = 0;
+    std::vector<int64_t> params;  // model order
+    std::vector<Bucket> buckets;
+    int64_t numel = 0, unpadded = 0, window_numel = 0, arena_numel = 0, shard_numel = 0;
+    std::vector<SegDesc> segs;
+    std::vector<TileDesc> tiles;
+    int32_t stats_grid = 0, apply_grid = 0;
+    int32_t partial_base = 0;
+    int64_t ws_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
+};
+
+// Workspace map (byte offsets).
+constexpr int64_t kWsState = 0;       // persistent scaler / step-count state
+constexpr int64_t kWsStepRec = 256;   // per-step scalars for the apply pass
+constexpr int64_t kWsStats = 1280;    // dopt_stats of the last step
+constexpr int64_t kWsRecord = 1536;   // grad-stats record {sumsq, zeros}
+constexpr int64_t kWsPartials = 1792; // per-workgroup partials of pass 1
+
+void set_error(int code, const std::string &msg);
+int fail(int code, const std::string &msg);
+
+}  // namespace dopt
+
+struct dopt_layout {
+    int32_t N = 1, r = 0;
+    int32_t max_hgroup = 0;
+    std::vector<dopt::Param> params;
+    std::vector<dopt::Buffer> buffers;
+    int64_t state_numel = 0;
+    int32_t total_partials = 0;
+    int64_t ws_bytes = 0;
+};

@@ -1,0 +1,314 @@
+// Host-side shard-range mapper: dopt_build_ranges and the layout queries.
+//
+// Pages cited: [DO] "Megatron-LM distrib_optimizer.py 源码精读";
+// [ZL] "02 · ZeRO 显存账本与 Megatron DistributedOptimizer";
+// [DP] "Megatron-LM distributed 包深度解析：DDP 梯度同步与 finalize_model_grads 全流程".
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "internal.h"
+
+namespace dopt {
+
+static thread_local std::string g_last_error;
+
+void set_error(int code, const std::string &msg) {
+    (void)code;
+    g_last_error = msg;
+}
+
+int fail(int code, const std::string &msg) {
+    set_error(code, msg);
+    return code;
+}
+
+static int64_t align_up(int64_t x, int64_t d) { return (x + d - 1) / d * d; }
+
+static bool valid_dtype(int32_t d) { return d == DOPT_F32 || d == DOPT_BF16 || d == DOPT_F16; }
+
+// Lay one flat buffer out in buckets ([DO] "Bucket 划分算法：逆序遍历 + 尺寸触发",
+// "两级 Padding 机制").  The cursor walks the params from the last one in model
+// order to the first (roughly the order their grads become ready in the
+// backward pass).  The size trigger compares the running bucket length
+// (param end minus bucket start) with bucket_size, so a single param larger
+// than bucket_size forms an oversized bucket of its own.
+static int lay_out_buffer(dopt_layout &L, Buffer &B, int64_t bucket_size, bool busbw) {
+    int64_t divisor = std::lcm<int64_t>(L.N, 128);
+    if (busbw) divisor = std::lcm<int64_t>(divisor, int64_t(1) << 16);
+
+    int64_t bucket_start = 0;
+    int32_t open = 0;  // params placed in the bucket being filled
+    // Ends the open bucket at element x: records its unpadded length, pads its
+    // end for an even N-way split and returns where the next bucket begins.
+    auto seal = [&](int64_t x) -> int64_t {
+        Bucket bk;
+        bk.offset = bucket_start;
+        bk.unpadded = x - bucket_start;
+        const int64_t end = align_up(x, divisor);
+        bk.numel = end - bucket_start;
+        bk.n_params = open;
+        B.buckets.push_back(bk);
+        bucket_start = end;
+        open = 0;
+        return end;
+    };
+
+    int64_t cursor = 0, last_end = 0;
+    for (auto it = B.params.rbegin(); it != B.params.rend(); ++it) {
+        Param &p = L.params[*it];
+        cursor = align_up(cursor, 64);  // 128-byte aligned start for 16-bit elements
+        if (p.newb && open > 0) cursor = seal(cursor);
+        p.start = cursor;
+        p.end = cursor + p.numel;
+        p.bucket = static_cast<int32_t>(B.buckets.size());
+        ++open;
+        last_end = p.end;
+        const bool full = bucket_size > 0 && (p.end - bucket_start) >= bucket_size;
+        cursor = (full || p.newb) ? seal(p.end) : p.end;
+    }
+    if (open > 0) seal(last_end);
+
+    B.numel = bucket_start;
+    B.unpadded = 0;
+    for (const Bucket &bk : B.buckets) B.unpadded += bk.unpadded;
+    // [DO] "最终内存大小断言" and "Bucket 级别的均等切分".
+    if (B.unpadded > B.numel) return fail(DOPT_ERR_ASSERT, "layout invariant: numel_unpadded <= numel");
+    if (B.numel % L.N != 0) return fail(DOPT_ERR_ASSERT, "layout invariant: numel % dp_size == 0");
+    for (const Bucket &bk : B.buckets)
+        if (bk.numel % L.N != 0) return fail(DOPT_ERR_ASSERT, "layout invariant: bucket numel % dp_size == 0");
+    return DOPT_OK;
+}
+
+// Rank r's window of every bucket and every param's intersection with it in
+// the four views of [DO] "Range 类：四种视角的统一抽象": first in window-local
+// coordinates, then shifted to the buffer, to the bucket and into the param.
+static void map_windows(dopt_layout &L, Buffer &B) {
+    int64_t arena = 0;
+    for (Bucket &bk : B.buckets) {
+        bk.shard = bk.numel / L.N;
+        bk.window_start = bk.offset + int64_t(L.r) * bk.shard;
+        bk.arena_offset = arena;
+        arena += bk.shard;
+    }
+    B.window_numel = arena;
+    B.arena_numel = align_up(std::max<int64_t>(arena, 1), kTile);
+    B.shard_numel = 0;
+    B.segs.clear();
+    for (int64_t pi : B.params) {
+        Param &p = L.params[pi];
+        const Bucket &bk = B.buckets[p.bucket];
+        const int64_t lo = std::max<int64_t>(0, p.start - bk.window_start);
+        const int64_t hi = std::min<int64_t>(bk.shard, p.end - bk.window_start);
+        if (hi <= lo) {
+            p.has_shard = 0;
+            continue;
+        }
+        p.has_shard = 1;
+        p.local = {lo, hi};
+        p.world = {lo + bk.window_start, hi + bk.window_start};
+        p.world_in_bucket = {p.world.start - bk.offset, p.world.end - bk.offset};
+        const int64_t sub = std::max<int64_t>(0, bk.window_start - p.start);
+        p.prange = {sub, sub + (hi - lo)};
+        p.arena = bk.arena_offset + lo;
+        B.shard_numel += hi - lo;
+        B.segs.push_back(SegDesc{p.arena, p.arena + (hi - lo), p.hgroup, 0});
+    }
+    std::sort(B.segs.begin(), B.segs.end(), [](const SegDesc &a, const SegDesc &b) { return a.start < b.start; });
+}
+
+// Tile table: for each TILE-element slice of the arena, the run of segments
+// that overlap it and whether one segment covers it entirely.
+static void build_tiles(Buffer &B) {
+    const int64_t n_tiles = B.arena_numel / kTile;
+    B.tiles.assign(static_cast<size_t>(n_tiles), TileDesc{0, 0});
+    const int64_t ns = static_cast<int64_t>(B.segs.size());
+    int64_t s = 0;
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int64_t lo = t * kTile, hi = lo + kTile;
+        while (s < ns && B.segs[s].end <= lo) ++s;
+        int64_t j = s;
+        while (j < ns && B.segs[j].start < hi) ++j;
+        const int32_t cnt = static_cast<int32_t>(j - s);
+        const bool full = cnt == 1 && B.segs[s].start <= lo && B.segs[s].end >= hi;
+        B.tiles[t] = TileDesc{static_cast<int32_t>(s), cnt | (full ? kTileFull : 0)};
+    }
+    B.stats_grid = static_cast<int32_t>(std::min<int64_t>(n_tiles, kStatsMaxBlocks));
+    B.apply_grid = static_cast<int32_t>(std::min<int64_t>(n_tiles, kApplyMaxBlocks));
+}
+
+static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg, dopt_layout &L) {
+    L.N = cfg->dp_size;
+    L.r = cfg->dp_rank;
+    L.params.resize(static_cast<size_t>(n));
+    for (int64_t i = 0; i < n; ++i) {
+        const dopt_param_desc &d = params[i];
+        if (d.numel <= 0 || !valid_dtype(d.param_dtype) || !valid_dtype(d.grad_dtype) || d.hgroup < 0 ||
+            d.hgroup >= DOPT_MAX_HGROUPS)
+            return fail(DOPT_ERR_INVALID, "param " + std::to_string(i) + ": bad numel, dtype or hgroup");
+        Param &p = L.params[i];
+        p.numel = d.numel;
+        p.pd = d.param_dtype;
+        p.gd = d.grad_dtype;
+        p.newb = d.requires_new_bucket != 0;
+        p.hgroup = d.hgroup;
+        L.max_hgroup = std::max(L.max_hgroup, d.hgroup);
+        // one flat buffer per (param dtype, grad dtype), first appearance first ([DP] §2.2 (3))
+        size_t k = 0;
+        while (k < L.buffers.size() && !(L.buffers[k].pd == p.pd && L.buffers[k].gd == p.gd)) ++k;
+        if (k == L.buffers.size()) {
+            L.buffers.emplace_back();
+            L.buffers.back().pd = p.pd;
+            L.buffers.back().gd = p.gd;
+        }
+        p.buffer = static_cast<int32_t>(k);
+        L.buffers[k].params.push_back(i);
+    }
+    int64_t ws = kWsPartials;
+    int32_t partials = 0;
+    for (Buffer &B : L.buffers) {
+        int rc = lay_out_buffer(L, B, cfg->bucket_size, cfg->pad_for_high_busbw != 0);
+        if (rc != DOPT_OK) return rc;
+        map_windows(L, B);
+        build_tiles(B);
+        B.partial_base = partials;
+        partials += B.stats_grid;
+        L.state_numel += B.shard_numel;
+    }
+    L.total_partials = partials;
+    ws += align_up(int64_t(partials) * 16, 256);
+    for (Buffer &B : L.buffers) {
+        B.ws_tiles = ws;
+        ws += align_up(int64_t(B.tiles.size()) * int64_t(sizeof(TileDesc)), 256);
+        B.ws_segs = ws;
+        ws += align_up(std::max<int64_t>(int64_t(B.segs.size()), 1) * int64_t(sizeof(SegDesc)), 256);
+    }
+    L.ws_bytes = ws;
+    return DOPT_OK;
+}
+
+}  // namespace dopt
+
+using namespace dopt;
+
+extern "C" {
+
+const char *dopt_last_error(void) { return g_last_error.c_str(); }
+
+int dopt_build_ranges(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg, dopt_layout **out) {
+    if (!params || !cfg || !out || n <= 0) return fail(DOPT_ERR_INVALID, "null argument or n <= 0");
+    *out = nullptr;
+    if (cfg->dp_size < 1 || cfg->dp_rank < 0 || cfg->dp_rank >= cfg->dp_size)
+        return fail(DOPT_ERR_INVALID, "dp_rank must satisfy 0 <= dp_rank < dp_size");
+    dopt_layout *L = new (std::nothrow) dopt_layout();
+    if (!L) return fail(DOPT_ERR_NOMEM, "out of host memory");
+    int rc;
+    try {
+        rc = build(params, n, cfg, *L);
+    } catch (const std::bad_alloc &) {
+        rc = fail(DOPT_ERR_NOMEM, "out of host memory");
+    }
+    if (rc != DOPT_OK) {
+        delete L;
+        return rc;
+    }
+    *out = L;
+    return DOPT_OK;
+}
+
+void dopt_layout_free(dopt_layout *layout) { delete layout; }
+
+int32_t dopt_layout_num_buffers(const dopt_layout *L) { return L ? static_cast<int32_t>(L->buffers.size()) : 0; }
+
+int dopt_layout_buffer(const dopt_layout *L, int32_t k, dopt_buffer_info *out) {
+    if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");
+    if (k < 0 || k >= static_cast<int32_t>(L->buffers.size())) return fail(DOPT_ERR_RANGE, "buffer index");
+    const Buffer &B = L->buffers[k];
+    out->param_dtype = B.pd;
+    out->grad_dtype = B.gd;
+    out->n_buckets = static_cast<int32_t>(B.buckets.size());
+    out->n_params = static_cast<int32_t>(B.params.size());
+    out->numel = B.numel;
+    out->numel_unpadded = B.unpadded;
+    out->window_numel = B.window_numel;
+    out->arena_numel = B.arena_numel;
+    out->shard_numel = B.shard_numel;
+    return DOPT_OK;
+}
+
+int dopt_layout_bucket(const dopt_layout *L, int32_t k, int32_t b, dopt_bucket_info *out) {
+    if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");
+    if (k < 0 || k >= static_cast<int32_t>(L->buffers.size()) || b < 0 ||
+        b >= static_cast<int32_t>(L->buffers[k].buckets.size()))
+        return fail(DOPT_ERR_RANGE, "bucket index");
+    const Bucket &bk = L->buffers[k].buckets[b];
+    out->offset = bk.offset;
+    out->numel = bk.numel;
+    out->numel_unpadded = bk.unpadded;
+    out->shard_size = bk.shard;
+    out->window_start = bk.window_start;
+    out->arena_offset = bk.arena_offset;
+    out->n_params = bk.n_params;
+    out->reserved = 0;
+    return DOPT_OK;
+}
+
+int dopt_layout_rank_window(const dopt_layout *L, int32_t k, int32_t b, int32_t rank, dopt_range *out) {
+    if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");
+    if (k < 0 || k >= static_cast<int32_t>(L->buffers.size()) || b < 0 ||
+        b >= static_cast<int32_t>(L->buffers[k].buckets.size()) || rank < 0 || rank >= L->N)
+        return fail(DOPT_ERR_RANGE, "bucket or rank index");
+    const Bucket &bk = L->buffers[k].buckets[b];
+    out->start = bk.offset + int64_t(rank) * bk.shard;
+    out->end = out->start + bk.shard;
+    return DOPT_OK;
+}
+
+int dopt_layout_param(const dopt_layout *L, int64_t p, dopt_param_info *out) {
+    if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");
+    if (p < 0 || p >= static_cast<int64_t>(L->params.size())) return fail(DOPT_ERR_RANGE, "param index");
+    const Param &q = L->params[p];
+    std::memset(out, 0, sizeof *out);
+    out->buffer = q.buffer;
+    out->bucket = q.bucket;
+    out->has_shard = q.has_shard;
+    out->hgroup = q.hgroup;
+    out->start = q.start;
+    out->end = q.end;
+    if (q.has_shard) {
+        out->gbuf_world = q.world;
+        out->gbuf_world_in_bucket = q.world_in_bucket;
+        out->gbuf_local = q.local;
+        out->param = q.prange;
+    }
+    out->arena_offset = q.has_shard ? q.arena : -1;
+    return DOPT_OK;
+}
+
+// [DO] group-building section; [ZL] §3: 16-bit params feed model_float16,
+// shard_float16 (the param-window view) and shard_fp32_from_float16 (the fp32
+// master); fp32 params feed model_fp32 and shard_fp32.  Only params with a
+// shard on this rank are listed.
+int64_t dopt_layout_group(const dopt_layout *L, int32_t kind, int32_t hgroup, int64_t *idx, int64_t cap) {
+    if (!L) return fail(DOPT_ERR_INVALID, "null layout");
+    if (kind < DOPT_GROUP_MODEL_FLOAT16 || kind > DOPT_GROUP_SHARD_FP32) return fail(DOPT_ERR_RANGE, "group kind");
+    const bool lowp = kind == DOPT_GROUP_MODEL_FLOAT16 || kind == DOPT_GROUP_SHARD_FLOAT16 ||
+                      kind == DOPT_GROUP_SHARD_FP32_FROM_FLOAT16;
+    int64_t count = 0;
+    for (size_t i = 0; i < L->params.size(); ++i) {
+        const Param &q = L->params[i];
+        if (!q.has_shard || q.hgroup != hgroup || (q.pd != DOPT_F32) != lowp) continue;
+        if (idx && count < cap) idx[count] = static_cast<int64_t>(i);
+        ++count;
+    }
+    return count;
+}
+
+int64_t dopt_layout_state_numel(const dopt_layout *L) { return L ? L->state_numel : 0; }
+
+int64_t dopt_workspace_bytes(const dopt_layout *L) { return L ? L->ws_bytes : 0; }
+
+int64_t dopt_stats_record_offset(const dopt_layout *L) { return L ? kWsRecord : 0; }
+
+}  // extern "C"

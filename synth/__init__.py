@@ -76,6 +76,14 @@ def buffer_stream(stream: int, buffer_index: int) -> int:
     return stream + _BUFFER_STRIDE * buffer_index
 
 
+def weight_stream(buffer_index: int) -> int:
+    return buffer_stream(STREAM_WEIGHT, buffer_index)
+
+
+def grad_stream(buffer_index: int) -> int:
+    return buffer_stream(STREAM_GRAD, buffer_index)
+
+
 _TORCH_DTYPES = None
 
 

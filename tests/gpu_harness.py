@@ -1,0 +1,394 @@
+"""Parity harness: runs the HIP path (through the C ABI) and the oracle on the
+same seeded inputs and compares them.
+
+Tolerances (fixed for this method): integer results bit-exact; fp32 master,
+m and v within max(1e-6 * |oracle|, 1e-9); grad norm within 1e-5 relative;
+16-bit params within 1 ulp.
+
+Inputs are keyed by (seed, stream, step, arena index): weights N(0, sigma_w)
+narrowed to the param dtype; per-step grads N(0, sigma_g) (times the loss
+scale the step's grads carry) narrowed to the grad dtype; optional exact
+zeros; optionally one +inf at a seeded shard element.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from tests.oracle_harness import OracleRun, to_bits
+
+MASTER_RTOL, MASTER_ATOL = 1e-6, 1e-9
+NORM_RTOL = 1e-5
+PARAM_ULPS = 1
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Case:
+    name: str
+    params: Sequence
+    dp_size: int
+    dp_rank: int
+    bucket_size: int = 0
+    busbw: int = 0
+    steps: int = 3
+    grad_sigma: float = 1e-2
+    weight_sigma: float = 0.02
+    zero_frac: float = 0.0
+    dynamic: bool = False
+    initial_scale: float = 1.0
+    inf_step: Optional[int] = None
+    inf_value: float = math.inf
+    seed: int = 0
+    hparams: List = field(default_factory=lambda: [(1e-3, 0.9, 0.999, 1e-8, 0.01)])
+    max_norm: float = 1.0
+    const_grad: Optional[float] = None  # all grads equal to this value
+
+    def scale_at(self, step: int) -> float:
+        if not self.dynamic:
+            return self.initial_scale
+        s = self.initial_scale
+        if self.inf_step is not None and step > self.inf_step:
+            s *= 0.5
+        return s
+
+
+def case_from_workload(w) -> Case:
+    return Case(w.name, synth.PARAM_LISTS[w.model](), w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw,
+                w.steps, w.grad_sigma, w.weight_sigma, w.zero_frac, w.dynamic_scale, w.initial_scale, w.inf_step,
+                seed=w.seed, hparams=[(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)], max_norm=w.max_grad_norm)
+
+
+# ---------------------------------------------------------------- inputs ----
+
+def host_weights(case: Case, k: int, dt: str, n: int, out=None):
+    return synth.fill_normal(dt, n, case.seed, synth.weight_stream(k), 0, case.weight_sigma,
+                             out=out)
+
+
+def host_grads(case: Case, k: int, dt: str, n: int, step: int, out=None):
+    if case.const_grad is not None:
+        t = out if out is not None else torch.empty(n, dtype=synth.torch_dtype(dt))
+        t.fill_(case.const_grad)
+        return t
+    return synth.fill_normal(dt, n, case.seed, synth.grad_stream(k), step, case.grad_sigma,
+                             scale=case.scale_at(step), zero_frac=case.zero_frac, out=out)
+
+
+def inf_position(case: Case, O: oracle.Layout):
+    """(buffer, arena index) of the seeded overflow element: the j-th shard element in buffer/arena order."""
+    total = sum(O.buffer(k)["shard_numel"] for k in range(O.num_buffers))
+    j = synth.uniform_index(case.seed, synth.STREAM_INF_POS, case.inf_step, 0, total)
+    for k in range(O.num_buffers):
+        s, ln, _ = O.segments(k)
+        if j < int(ln.sum()):
+            c = np.cumsum(ln)
+            q = int(np.searchsorted(c, j, side="right"))
+            before = int(c[q - 1]) if q > 0 else 0
+            return k, int(s[q]) + (j - before)
+        j -= int(ln.sum())
+    raise AssertionError("no shard element")
+
+
+# ------------------------------------------------------------ comparisons ---
+
+def ulp_dist(a_bits: np.ndarray, b_bits: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "f32":
+        a = a_bits.view(np.int32).astype(np.int64)
+        b = b_bits.view(np.int32).astype(np.int64)
+        sign = np.int64(1 << 31)
+        mag = np.int64(0x7fffffff)
+    else:
+        a = a_bits.view(np.uint16).astype(np.int64)
+        b = b_bits.view(np.uint16).astype(np.int64)
+        sign = np.int64(0x8000)
+        mag = np.int64(0x7fff)
+    oa = np.where(a & sign, -(a & mag), a & mag)
+    ob = np.where(b & sign, -(b & mag), b & mag)
+    return np.abs(oa - ob)
+
+
+def check_f32(name: str, dev: np.ndarray, ref: np.ndarray) -> dict:
+    dev = dev.astype(np.float64)
+    ref = ref.astype(np.float64)
+    err = np.abs(dev - ref)
+    tol = np.maximum(MASTER_RTOL * np.abs(ref), MASTER_ATOL)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} outside tolerance; idx {i} dev {dev[i]} ref {ref[i]}")
+    return {"n": int(dev.size), "bit_exact": float(np.mean(dev == ref)) if dev.size else 1.0,
+            "max_rel": float(np.max(err / np.maximum(np.abs(ref), 1e-30))) if dev.size else 0.0}
+
+
+def check_param(name: str, dev_bits: np.ndarray, ref_bits: np.ndarray, dt: str) -> dict:
+    d = ulp_dist(dev_bits, ref_bits, dt)
+    if d.size and d.max() > PARAM_ULPS:
+        i = np.flatnonzero(d > PARAM_ULPS)[:5]
+        raise AssertionError(f"{name}: {int((d > PARAM_ULPS).sum())} params beyond {PARAM_ULPS} ulp; idx {i}")
+    return {"n": int(d.size), "bit_exact": float(np.mean(d == 0)) if d.size else 1.0, "max_ulp": int(d.max()) if d.size else 0}
+
+
+def check_stats(dev: dict, ref: oracle.Stats, step: int):
+    where = f"step {step}"
+    assert dev["found_inf"] == ref.found_inf, where
+    assert dev["skipped"] == ref.skipped, where
+    assert dev["step_count"] == ref.t, where
+    assert dev["num_zeros"] == ref.zeros, (where, dev["num_zeros"], ref.zeros)
+    assert dev["loss_scale_used"] == ref.scale_used and dev["loss_scale_next"] == ref.scale_next, where
+    if math.isfinite(ref.sumsq):
+        assert math.isclose(dev["grad_norm"], ref.norm, rel_tol=NORM_RTOL, abs_tol=0.0) or \
+            (ref.norm == 0.0 and dev["grad_norm"] == 0.0), (where, dev["grad_norm"], ref.norm)
+        assert dev["clip_applied"] == ref.clip_applied, where
+        if ref.clip_applied:
+            assert math.isclose(dev["clip_coef"], ref.clip_coef, rel_tol=NORM_RTOL), where
+    else:
+        assert not math.isfinite(dev["sumsq"]), where
+
+
+# ---------------------------------------------------------------- device ----
+
+def _dopt():
+    import sharded_mixed_precision_amd as D
+    return D
+
+
+class DeviceRun:
+    def __init__(self, case: Case):
+        D = _dopt()
+        from sharded_mixed_precision_amd.arena import DeviceArenas
+        self.D = D
+        self.L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw)
+        self.A = DeviceArenas(self.L)
+        self.stream = torch.cuda.current_stream()
+        self.case = case
+
+    def init(self, host_params: List[torch.Tensor]):
+        for k, t in enumerate(host_params):
+            self.A.bufs[k]["param"].copy_(t)
+        c = self.case
+        sc = self.D.scaler_cfg(c.dynamic, c.initial_scale)
+        self.D.dopt_init_state(self.L, self.A.bufs, sc, self.A.workspace, self.stream)
+
+    def step(self, host_grads: List[torch.Tensor], split: bool = False) -> dict:
+        for k, t in enumerate(host_grads):
+            self.A.bufs[k]["grad"].copy_(t)
+        c = self.case
+        if split:
+            self.D.dopt_step_stats(self.L, self.A.bufs, self.A.workspace, self.stream)
+            self.D.dopt_step_finalize(self.L, c.hparams, c.max_norm, self.A.workspace, self.stream)
+            self.D.dopt_step_apply(self.L, self.A.bufs, self.A.workspace, self.stream)
+            return self.D.dopt_read_stats(self.L, self.A.workspace, self.stream)
+        return self.D.dopt_step(self.L, self.A.bufs, c.hparams, c.max_norm, self.A.workspace, self.stream)
+
+    def host(self, k: int, key: str) -> np.ndarray:
+        t = self.A.bufs[k][key]
+        return to_bits(t.cpu())
+
+    def gather(self, k: int, key: str, idx_dev: torch.Tensor) -> np.ndarray:
+        t = self.A.bufs[k][key]
+        return to_bits(t.index_select(0, idx_dev).cpu())
+
+
+# ------------------------------------------------------------ full parity ---
+
+def run_full(case: Case, split_steps: Sequence[int] = ()) -> List[dict]:
+    """Every element compared after every step."""
+    t0 = time.time()
+    dev = DeviceRun(case)
+    arena = [dev.L.buffer(k)["arena_numel"] for k in range(dev.L.num_buffers)]
+    orc = OracleRun(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, arena_numel=arena)
+    for k in range(orc.nb):
+        w = orc.L.buffer(k)["window_numel"]
+        assert arena[k] == -(-max(w, 1) // dev.D.DOPT_ARENA_ALIGN) * dev.D.DOPT_ARENA_ALIGN
+    orc.scaler = oracle.make_scaler(case.dynamic, case.initial_scale)
+    hp = [orc.bufs[k] for k in range(orc.nb)]
+    params0 = []
+    for k, b in enumerate(hp):
+        t = host_weights(case, k, b["pd"], b["n"])
+        b["param"][:] = to_bits(t)
+        params0.append(t)
+    dev.init(params0)
+    orc.init_state()
+    masks = [orc.valid(k) for k in range(orc.nb)]
+    init_bits = [to_bits(p).copy() for p in params0]
+    pos = inf_position(case, orc.L) if case.inf_step else None
+    report = []
+    for s in range(1, case.steps + 1):
+        grads = []
+        for k, b in enumerate(hp):
+            g = host_grads(case, k, b["gd"], b["n"], s)
+            if pos is not None and s == case.inf_step and pos[0] == k:
+                g[pos[1]] = case.inf_value
+            b["grad"][:] = to_bits(g)
+            grads.append(g)
+        ref = orc.step(case.hparams, case.max_norm)
+        got = dev.step(grads, split=s in split_steps)
+        check_stats(got, ref, s)
+        rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": ref.norm}
+        for k, b in enumerate(hp):
+            m = masks[k]
+            if b["pd"] != "f32":
+                rep[f"master{k}"] = check_f32(f"{case.name} step {s} master[{k}]", dev.host(k, "master")[m],
+                                              b["master"][m])
+            rep[f"m{k}"] = check_f32(f"{case.name} step {s} m[{k}]", dev.host(k, "exp_avg")[m], b["m"][m])
+            rep[f"v{k}"] = check_f32(f"{case.name} step {s} v[{k}]", dev.host(k, "exp_avg_sq")[m], b["v"][m])
+            pdev = dev.host(k, "param")
+            rep[f"param{k}"] = check_param(f"{case.name} step {s} param[{k}]", pdev[m], b["param"][m], b["pd"])
+            # slots that hold no param element are never written
+            assert np.array_equal(pdev[~m], init_bits[k][~m]), f"step {s}: param arena gap written"
+        report.append(rep)
+    log(f"[parity] {case.name}: {case.steps} steps full compare ok in {time.time() - t0:.1f}s; last {report[-1]}")
+    return report
+
+
+# --------------------------------------------------------- sampled parity ---
+
+def _pick_samples(O: oracle.Layout, k: int, n_rand: int, seed: int) -> np.ndarray:
+    s, ln, _ = O.segments(k)
+    if len(s) == 0:
+        return np.zeros(0, np.int64)
+    c = np.cumsum(ln)
+    total = int(c[-1])
+    rng = np.random.default_rng(seed + 17 * k)
+    j = rng.integers(0, total, size=min(n_rand, total))
+    q = np.searchsorted(c, j, side="right")
+    before = np.where(q > 0, c[np.maximum(q - 1, 0)], 0)
+    idx = s[q] + (j - before)
+    # every segment's first and last element, and the elements around each
+    # 2048-element tile boundary inside the first segments
+    edges = np.concatenate([s, s + ln - 1])
+    tb = []
+    for a, b in zip(s[:8].tolist(), (s + ln)[:8].tolist()):
+        t = (a // 2048 + 1) * 2048
+        while t < b and len(tb) < 256:
+            tb += [t - 1, t]
+            t += 2048 * 97
+    return np.unique(np.concatenate([idx, edges, np.array(tb, np.int64)]).astype(np.int64))
+
+
+def oracle_stats_parallel(O: oracle.Layout, grads: List[torch.Tensor], inv_scale: float, workers: int = 16,
+                          chunk: int = 1 << 26) -> oracle.Stats:
+    """The oracle's S2 over all shard elements, split into disjoint arena
+    ranges run on host threads (each range is one plain single-threaded oracle
+    call); partials are added in range order."""
+    lib = oracle.lib()
+    jobs = []
+    for k, g in enumerate(grads):
+        n = g.numel()
+        for lo in range(0, n, chunk):
+            jobs.append((k, lo, min(lo + chunk, n)))
+
+    def run(job):
+        k, lo, hi = job
+        st = oracle.Stats()
+        lib.or_grad_stats_range(O.handle, k, grads[k].data_ptr(), inv_scale, lo, hi, ctypes.byref(st))
+        return st.sumsq, st.zeros, st.found_inf
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(run, jobs))
+    out = oracle.Stats()
+    out.sumsq = 0.0
+    for sq, z, fi in parts:
+        out.sumsq += sq
+        out.zeros += z
+        out.found_inf |= fi
+    return out
+
+
+def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
+    """Full-size run on the device; the oracle computes the exact per-step
+    stats over all shard elements and the trajectories of sampled elements."""
+    t0 = time.time()
+    lib = oracle.lib()
+    dev = DeviceRun(case)
+    O = oracle.Layout(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw)
+    nb = O.num_buffers
+    infos = []
+    for k in range(nb):
+        b = O.buffer(k)
+        pd, gd = {0: "f32", 1: "bf16", 2: "f16"}[b["param_dtype"]], {0: "f32", 1: "bf16", 2: "f16"}[b["grad_dtype"]]
+        n = dev.L.buffer(k)["arena_numel"]
+        assert n == -(-max(b["window_numel"], 1) // 2048) * 2048
+        infos.append((pd, gd, n))
+    samples, hgs, dev_idx = [], [], []
+    st_master, st_m, st_v, st_param = [], [], [], []
+    params0 = []
+    for k, (pd, gd, n) in enumerate(infos):
+        p = host_weights(case, k, pd, n)
+        params0.append(p)
+        idx = _pick_samples(O, k, n_samples, case.seed)
+        samples.append(idx)
+        hgs.append(O.hgroup_at(k, idx).astype(np.int32))
+        dev_idx.append(torch.from_numpy(idx).cuda())
+        pbits = to_bits(p)[idx].copy()
+        mas = np.zeros(idx.size, np.float32)
+        if pd == "bf16":
+            lib.or_bf16_to_f32_n(pbits.ctypes.data, mas.ctypes.data, idx.size)
+        elif pd == "f16":
+            lib.or_f16_to_f32_n(pbits.ctypes.data, mas.ctypes.data, idx.size)
+        else:
+            mas[:] = pbits.view(np.float32)
+        st_master.append(mas)
+        st_m.append(np.zeros(idx.size, np.float32))
+        st_v.append(np.zeros(idx.size, np.float32))
+        st_param.append(pbits.copy())
+    dev.init(params0)
+    del params0
+    log(f"[parity] {case.name}: init done {time.time() - t0:.1f}s, samples {[s.size for s in samples]}")
+    scaler = oracle.make_scaler(case.dynamic, case.initial_scale)
+    t = ctypes.c_int64(0)
+    hpa = oracle.make_hparams(case.hparams)
+    pos = inf_position(case, O) if case.inf_step else None
+    grads = [torch.empty(n, dtype=synth.torch_dtype(gd)) for (pd, gd, n) in infos]
+    report = []
+    for s in range(1, case.steps + 1):
+        ts = time.time()
+        for k, (pd, gd, n) in enumerate(infos):
+            host_grads(case, k, gd, n, s, out=grads[k])
+            if pos is not None and s == case.inf_step and pos[0] == k:
+                grads[k][pos[1]] = case.inf_value
+        tg = time.time()
+        st = oracle_stats_parallel(O, grads, float(np.float32(1.0 / scaler.scale)))
+        sc = oracle.Scalars()
+        assert lib.or_decide(ctypes.byref(st), ctypes.byref(scaler), ctypes.byref(t), hpa, len(case.hparams),
+                             case.max_norm, ctypes.byref(sc)) == 0
+        for k, (pd, gd, n) in enumerate(infos):
+            gs = np.ascontiguousarray(to_bits(grads[k])[samples[k]])
+            lib.or_apply_elems(oracle.DTYPES[pd], oracle.DTYPES[gd], samples[k].size, hgs[k].ctypes.data,
+                               gs.ctypes.data, st_master[k].ctypes.data, st_m[k].ctypes.data, st_v[k].ctypes.data,
+                               st_param[k].ctypes.data, ctypes.byref(sc))
+        to = time.time()
+        got = dev.step(grads)
+        check_stats(got, st, s)
+        rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": st.norm, "skipped": got["skipped"]}
+        for k, (pd, gd, n) in enumerate(infos):
+            if pd != "f32":
+                rep[f"master{k}"] = check_f32(f"{case.name} s{s} master[{k}]", dev.gather(k, "master", dev_idx[k]),
+                                              st_master[k])
+            rep[f"m{k}"] = check_f32(f"{case.name} s{s} m[{k}]", dev.gather(k, "exp_avg", dev_idx[k]), st_m[k])
+            rep[f"v{k}"] = check_f32(f"{case.name} s{s} v[{k}]", dev.gather(k, "exp_avg_sq", dev_idx[k]), st_v[k])
+            pdev = dev.gather(k, "param", dev_idx[k])
+            if pd == "f32":
+                rep[f"param{k}"] = check_f32(f"{case.name} s{s} param[{k}]", pdev, st_master[k])
+            else:
+                rep[f"param{k}"] = check_param(f"{case.name} s{s} param[{k}]", pdev, st_param[k], pd)
+        report.append(rep)
+        log(f"[parity] {case.name} step {s}: gen {tg - ts:.1f}s oracle {to - tg:.1f}s device+check "
+            f"{time.time() - to:.1f}s; {rep}")
+    log(f"[parity] {case.name}: sampled compare ok in {time.time() - t0:.1f}s")
+    return report

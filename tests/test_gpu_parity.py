@@ -1,0 +1,151 @@
+"""GPU parity: the HIP path (called through the C ABI) against the oracle.
+
+Tiny and GPT-2-small are compared element by element after every step; the
+three multi-billion-byte workloads run at full size on the device, with the
+oracle computing the exact per-step statistics over every shard element and
+the trajectories of about a million sampled elements per buffer (plus every
+segment's first and last element).  Edge cases: windows that start at odd
+offsets, empty windows, mixed dtypes and hyper-groups, lone-param buckets,
+bus-bandwidth padding, all-zero grads, NaN / -inf overflow, clipping on and
+off, the three-call split API, and run-to-run determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.models import ParamSpec
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    H.log(f"[gpu-test] start {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def test_tiny_workload_full():
+    H.run_full(H.case_from_workload(synth.WORKLOADS["tiny"]))
+
+
+def test_gpt2_small_workload_full():
+    rep = H.run_full(H.case_from_workload(synth.WORKLOADS["gpt2-small"]))
+    assert rep[-1]["param0"]["n"] == 15_554_976
+
+
+@pytest.mark.timeout(600)
+def test_llama3_8b_workload_sampled():
+    H.run_sampled(H.case_from_workload(synth.WORKLOADS["llama3-8b"]))
+
+
+@pytest.mark.timeout(900)
+def test_dense_7b_workload_sampled():
+    rep = H.run_sampled(H.case_from_workload(synth.WORKLOADS["dense-7b"]))
+    assert [r["skipped"] for r in rep] == [0, 0, 1, 0, 0]
+
+
+@pytest.mark.timeout(600)
+def test_llama3_70b_workload_sampled():
+    H.run_sampled(H.case_from_workload(synth.WORKLOADS["llama3-70b"]))
+
+
+@pytest.mark.parametrize("rank", [0, 5, 37, 63])
+def test_unaligned_windows(rank):
+    params = [ParamSpec("a", 384, "bf16", "bf16"), ParamSpec("b", 321, "bf16", "bf16")]
+    H.run_full(H.Case(f"unaligned-r{rank}", params, 64, rank, steps=3))
+
+
+@pytest.mark.parametrize("rank", [0, 77, 127])
+def test_odd_shards_many_buckets(rank):
+    params = [ParamSpec(f"p{i}", n, "bf16", "bf16") for i, n in enumerate([1000, 77, 4097, 3, 20000, 9, 131])]
+    H.run_full(H.Case(f"odd-r{rank}", params, 128, rank, bucket_size=2000, steps=3))
+
+
+def test_mixed_dtypes_hgroups_lone_buckets():
+    params = [ParamSpec("emb", 50000, "bf16", "f32", 1, 0), ParamSpec("w1", 7000, "bf16", "f32", 0, 0),
+              ParamSpec("n1", 256, "f32", "f32", 0, 1), ParamSpec("h1", 3333, "f16", "f16", 0, 2),
+              ParamSpec("w2", 12345, "bf16", "f32", 0, 1), ParamSpec("h2", 999, "f16", "f32", 0, 0),
+              ParamSpec("n2", 100, "f32", "f32", 0, 0)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
+    H.run_full(H.Case("mixed", params, 3, 1, bucket_size=5000, steps=4, hparams=hps))
+
+
+def test_high_busbw_padding():
+    params = [ParamSpec("a", 100_000, "bf16", "bf16"), ParamSpec("b", 3000, "bf16", "bf16")]
+    H.run_full(H.Case("busbw", params, 8, 6, busbw=1, steps=2))
+
+
+def test_empty_window():
+    # one 64-element param at N=4: numel pads to 128, ranks 2 and 3 own only padding
+    params = [ParamSpec("a", 64, "bf16", "bf16")]
+    for r in (2, 3):
+        rep = H.run_full(H.Case(f"empty-r{r}", params, 4, r, steps=2))
+        assert rep[-1]["param0"]["n"] == 0 and rep[-1]["norm_dev"] == 0.0
+
+
+def test_all_zero_grads():
+    params = [ParamSpec("a", 70000, "bf16", "bf16"), ParamSpec("b", 500, "bf16", "bf16")]
+    rep = H.run_full(H.Case("zeros", params, 2, 1, steps=2, const_grad=0.0))
+    assert rep[-1]["norm_dev"] == 0.0
+
+
+@pytest.mark.parametrize("bad", [math.nan, -math.inf, math.inf])
+def test_overflow_skips_step(bad):
+    params = [ParamSpec("a", 40000, "f16", "f16"), ParamSpec("b", 1000, "f16", "f16")]
+    H.run_full(H.Case("overflow", params, 2, 0, steps=4, dynamic=True, initial_scale=1024.0, inf_step=2,
+                      inf_value=bad, grad_sigma=1e-3))
+
+
+def test_clip_off_and_clip_active():
+    params = [ParamSpec("a", 30000, "bf16", "bf16")]
+    H.run_full(H.Case("noclip", params, 1, 0, steps=2, max_norm=0.0, grad_sigma=1.0))
+    H.run_full(H.Case("bigclip", params, 1, 0, steps=2, max_norm=1.0, grad_sigma=1.0))
+    H.run_full(H.Case("noclip-small", params, 1, 0, steps=2, max_norm=1.0, grad_sigma=1e-5))
+
+
+def test_split_api_matches_one_call():
+    params = [ParamSpec("a", 9000, "bf16", "bf16"), ParamSpec("n", 64, "f32", "f32")]
+    H.run_full(H.Case("split", params, 4, 2, steps=3), split_steps=(1, 3))
+
+
+def test_deterministic():
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.steps = 2
+    outs = []
+    for _ in range(2):
+        dev = H.DeviceRun(case)
+        nb = dev.L.num_buffers
+        params0 = [H.host_weights(case, k, "bf16", dev.L.buffer(k)["arena_numel"]) for k in range(nb)]
+        dev.init(params0)
+        stats = []
+        for s in (1, 2):
+            g = [H.host_grads(case, k, "bf16", dev.L.buffer(k)["arena_numel"], s) for k in range(nb)]
+            stats.append(dev.step(g))
+        outs.append((stats, [dev.host(0, key) for key in ("master", "exp_avg", "exp_avg_sq", "param")]))
+    assert outs[0][0] == outs[1][0]
+    for a, b in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(a, b)
+
+
+def test_argument_errors_are_reported():
+    import sharded_mixed_precision_amd as D
+    from sharded_mixed_precision_amd.arena import DeviceArenas
+    params = [ParamSpec("a", 5000, "bf16", "bf16", 0, 1)]
+    L = D.dopt_build_ranges(params, 2, 0)
+    A = DeviceArenas(L)
+    stream = torch.cuda.current_stream()
+    D.dopt_init_state(L, A.bufs, D.scaler_cfg(), A.workspace, stream)
+    with pytest.raises(D.DoptError) as e:  # hgroup 1 needs two hparam sets
+        D.dopt_step(L, A.bufs, [(1e-3, 0.9, 0.999, 1e-8, 0.0)], 1.0, A.workspace, stream)
+    assert e.value.code == -1
+    bad = dict(A.bufs[0])
+    bad["grad"] = A.bufs[0]["grad"][1:]  # 2-byte offset: not 256-byte aligned
+    with pytest.raises(D.DoptError):
+        D.dopt_step(L, [bad], [(1e-3, 0.9, 0.999, 1e-8, 0.0)] * 2, 1.0, A.workspace, stream)
+    with pytest.raises(D.DoptError):
+        D.dopt_init_state(L, A.bufs, D.scaler_cfg(True, 0.0), A.workspace, stream)
