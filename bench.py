@@ -1,9 +1,10 @@
 """Benchmark of the shard-local mixed-precision AdamW step on one MI355X.
 
-A step is one pass of the whole hot path over one rank's shard: pass 1
-(unscale, inf/NaN, sum of squares, zero count), the fixed-order reduction,
-the finalize (skip, norm, clip, loss scale, step count) and pass 2 (clip +
-AdamW + bias correction + write-back).  Inputs are synthetic (seeded
+A step is one pass of the whole hot path over one rank's shard, exactly what
+dopt_step runs: pass 1 (unscale, inf/NaN, sum of squares, zero count) with
+the fixed-order reduction and the finalize (skip, norm, clip, loss scale,
+step count) fused into its last workgroup, then pass 2 (clip + AdamW + bias
+correction + write-back).  Inputs are synthetic (seeded
 model-shaped param lists) and resident in HBM before the timed region.
 
 Prints one JSON line.  The default workload is a GPT-2-small-shaped param
@@ -29,7 +30,11 @@ ES = {"f32": 4, "bf16": 2, "f16": 2}
 # HBM traffic of k_apply measured with rocprofv3 PMC counters (FETCH_SIZE,
 # WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
 # reported only while the kernel source is the one that was measured.
-MEASURED_TRAFFIC = {}
+# bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
+# factors read off a 1 GiB fp32 copy.
+MEASURED_TRAFFIC = {
+    "gpt2-small": {"src": "acfdf444e3c28130", "bytes_per_launch": 451048940},
+}
 
 
 def _src_sha() -> str:
@@ -122,6 +127,9 @@ def main():
     ap.add_argument("--workload", default="gpt2-small")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="instead of the step: copy an fp32 buffer of this many MiB (a plain copy of known size, "
+                         "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the step; runs on more than one GPU are not supported.",
@@ -129,6 +137,23 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        ev[0].record()
+        reps = 5
+        for _ in range(reps):
+            dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        print(json.dumps({"calibration": "fp32 copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "ms": round(ms, 5), "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
     import synth
     import sharded_mixed_precision_amd as D
     from sharded_mixed_precision_amd.arena import DeviceArenas
@@ -154,9 +179,10 @@ def main():
     bufs_c = D.tensors(A.bufs)
     hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
 
+    # dopt_step = dopt_step_prepare + dopt_step_apply; the two halves are
+    # called here so that events can bracket the apply pass.
     def step(ev_a=None, ev_b=None):
-        D.dopt_step_stats(L, bufs_c, A.workspace, stream)
-        D.dopt_step_finalize(L, hp_c, w.max_grad_norm, A.workspace, stream)
+        D.dopt_step_prepare(L, bufs_c, hp_c, w.max_grad_norm, A.workspace, stream)
         if ev_a is not None:
             ev_a.record(stream)
         D.dopt_step_apply(L, bufs_c, A.workspace, stream)

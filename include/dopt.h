@@ -241,8 +241,9 @@ typedef struct dopt_stats {
  * [DO] "三层继承体系" (second layer): grads to fp32 + unscale + inf/NaN check,
  * clip by the global norm, then the inner AdamW step and the copy of the
  * masters back to the 16-bit params ([DO] "分片切片逻辑"; [DS] §2 step).
- * Equivalent to dopt_step_stats, dopt_step_finalize and dopt_step_apply in
- * that order.  A step with an inf/NaN grad is skipped: master, moments,
+ * Equivalent to dopt_step_prepare followed by dopt_step_apply (and to
+ * dopt_step_stats, dopt_step_finalize, dopt_step_apply in that order).  A
+ * step with an inf/NaN grad is skipped: master, moments,
  * params and the step count stay as they were, and a dynamic loss scale
  * backs off.  Skipping is not an error.
  *
@@ -253,6 +254,16 @@ typedef struct dopt_stats {
  */
 int dopt_step(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const dopt_hparams *hp,
               int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream, dopt_stats *out);
+
+/*
+ * dopt_step_prepare -- the first half of dopt_step for a single rank: pass 1
+ * (unscale, sum of squares, zero count; one launch per flat buffer), then
+ * one small launch that does the fixed-order reduction and the finalize
+ * below together.  Named after the prepare-grads phase of [DO] "三层继承体系"
+ * (second layer).  Arguments and errors as dopt_step; never synchronizes.
+ */
+int dopt_step_prepare(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const dopt_hparams *hp,
+                      int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream);
 
 /*
  * The step in three parts.  Between dopt_step_stats and dopt_step_finalize a

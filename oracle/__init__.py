@@ -152,12 +152,13 @@ class Layout:
         if rc != 0:
             raise OracleError(L.or_error().decode())
         self._h = h
+        self._free = L.or_free  # kept so that freeing works during interpreter shutdown
         self.dp_size, self.dp_rank, self.n_params = dp_size, dp_rank, n
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and _lib is not None:
-            _lib.or_free(h)
+        if h is not None:
+            self._free(h)
             self._h = None
 
     @property

@@ -114,6 +114,7 @@ def _load():
         "dopt_workspace_bytes": ([VP], I64),
         "dopt_init_state": ([VP, P(dopt_buffer_tensors), P(dopt_scaler_cfg), VP, VP], ctypes.c_int),
         "dopt_step": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP, P(dopt_stats)], ctypes.c_int),
+        "dopt_step_prepare": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_stats": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
@@ -131,7 +132,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", "dopt_layout_buffer",
             "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
-            "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_stats",
+            "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_prepare", "dopt_step_stats",
             "dopt_step_finalize", "dopt_step_apply", "dopt_stats_record_offset", "dopt_read_stats",
             "dopt_last_error")
 
@@ -166,12 +167,13 @@ class Layout:
 
     def __init__(self, handle: ctypes.c_void_p, dp_size: int, dp_rank: int, n_params: int):
         self._h = handle
+        self._free = _lib.dopt_layout_free  # kept so that freeing works during interpreter shutdown
         self.dp_size, self.dp_rank, self.n_params = dp_size, dp_rank, n_params
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None:
-            _lib.dopt_layout_free(h)
+            self._free(h)
             self._h = None
 
     @property
@@ -283,6 +285,12 @@ def dopt_step(layout: Layout, bufs, hparams: Sequence, max_grad_norm: float, wor
     _check(_lib.dopt_step(layout.handle, t, hp, len(hparams), max_grad_norm, _addr(workspace), _stream(stream),
                           ctypes.byref(st) if st is not None else None))
     return st.as_dict() if st is not None else None
+
+
+def dopt_step_prepare(layout: Layout, bufs, hparams, max_grad_norm: float, workspace, stream=None):
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
+    _check(_lib.dopt_step_prepare(layout.handle, t, hp, len(hp), max_grad_norm, _addr(workspace), _stream(stream)))
 
 
 def dopt_step_stats(layout: Layout, bufs, workspace, stream=None):

@@ -22,6 +22,9 @@ static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile si
 // device it runs on.
 constexpr int kStatsMaxBlocks = 1024;
 constexpr int kApplyMaxBlocks = 2048;
+// Tiles in flight per workgroup iteration of pass 1 (more bytes outstanding
+// per wave for a pass that only reads).
+constexpr int kStatsUnroll = 4;
 
 // Tile descriptor: the param segments that overlap the tile.
 constexpr int32_t kTileFull = 1 << 30;   // the tile lies inside one segment

@@ -68,30 +68,41 @@ struct InitArgs {
 
 // ---- element I/O -----------------------------------------------------------
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load; NT marks the line as streamed (read once), which lets the
+// memory system keep it out of the caches.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    if (NT) return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    return *static_cast<const u32x4 *>(p);
+}
+
 template <int DT>
 struct Elem;
 
 template <>
 struct Elem<DOPT_BF16> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const u32x4 u = ld16<NT>(static_cast<const uint16_t *>(base) + i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = __uint_as_float(w[j] << 16);
-            x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            x[2 * j] = __uint_as_float(u[j] << 16);
+            x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
         }
     }
     static __device__ __forceinline__ uint32_t bits(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
     }
     static __device__ __forceinline__ void store8(void *base, int64_t i, const float (&x)[kVec]) {
-        uint4 u;
-        u.x = bits(x[0]) | (bits(x[1]) << 16);
-        u.y = bits(x[2]) | (bits(x[3]) << 16);
-        u.z = bits(x[4]) | (bits(x[5]) << 16);
-        u.w = bits(x[6]) | (bits(x[7]) << 16);
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + i) = u;
+        u32x4 u;
+        u[0] = bits(x[0]) | (bits(x[1]) << 16);
+        u[1] = bits(x[2]) | (bits(x[3]) << 16);
+        u[2] = bits(x[4]) | (bits(x[5]) << 16);
+        u[3] = bits(x[6]) | (bits(x[7]) << 16);
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + i) = u;
     }
     static __device__ __forceinline__ void store1(void *base, int64_t i, float x) {
         static_cast<uint16_t *>(base)[i] = static_cast<uint16_t>(bits(x));
@@ -103,47 +114,52 @@ struct Elem<DOPT_F16> {
     static __device__ __forceinline__ float up(uint32_t h) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
     }
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const u32x4 u = ld16<NT>(static_cast<const uint16_t *>(base) + i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = up(w[j] & 0xffffu);
-            x[2 * j + 1] = up(w[j] >> 16);
+            x[2 * j] = up(u[j] & 0xffffu);
+            x[2 * j + 1] = up(u[j] >> 16);
         }
     }
     static __device__ __forceinline__ uint32_t bits(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
     }
     static __device__ __forceinline__ void store8(void *base, int64_t i, const float (&x)[kVec]) {
-        uint4 u;
-        u.x = bits(x[0]) | (bits(x[1]) << 16);
-        u.y = bits(x[2]) | (bits(x[3]) << 16);
-        u.z = bits(x[4]) | (bits(x[5]) << 16);
-        u.w = bits(x[6]) | (bits(x[7]) << 16);
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + i) = u;
+        u32x4 u;
+        u[0] = bits(x[0]) | (bits(x[1]) << 16);
+        u[1] = bits(x[2]) | (bits(x[3]) << 16);
+        u[2] = bits(x[4]) | (bits(x[5]) << 16);
+        u[3] = bits(x[6]) | (bits(x[7]) << 16);
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + i) = u;
     }
     static __device__ __forceinline__ void store1(void *base, int64_t i, float x) {
         static_cast<uint16_t *>(base)[i] = static_cast<uint16_t>(bits(x));
     }
 };
 
+template <bool NT = false>
 __device__ __forceinline__ void load8f(const float *base, int64_t i, float (&x)[kVec]) {
-    const float4 a = *reinterpret_cast<const float4 *>(base + i);
-    const float4 b = *reinterpret_cast<const float4 *>(base + i + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    const u32x4 a = ld16<NT>(base + i);
+    const u32x4 b = ld16<NT>(base + i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[j] = __uint_as_float(a[j]);
+        x[4 + j] = __uint_as_float(b[j]);
+    }
 }
 
 __device__ __forceinline__ void store8f(float *base, int64_t i, const float (&x)[kVec]) {
-    *reinterpret_cast<float4 *>(base + i) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(base + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    *reinterpret_cast<f32x4 *>(base + i) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4 *>(base + i + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
 template <>
 struct Elem<DOPT_F32> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
-        load8f(static_cast<const float *>(base), i, x);
+        load8f<NT>(static_cast<const float *>(base), i, x);
     }
     static __device__ __forceinline__ void store8(void *base, int64_t i, const float (&x)[kVec]) {
         store8f(static_cast<float *>(base), i, x);
@@ -159,6 +175,84 @@ __device__ __forceinline__ int owner_hgroup(const SegDesc *__restrict__ segs, in
     return -1;
 }
 
+// ---- finalize: skip, norm, clip, loss scale, step count, AdamW scalars ------
+//
+// [DO] "三层继承体系": an overflow skips the inner step; clipping uses the
+// global norm.  [DS] §3 config: dynamic loss scale starting at 2^16.  Clip
+// coefficient max_norm / (norm + 1e-6), applied when below 1; the dynamic
+// scale backs off (after `hysteresis` overflows) and grows every
+// growth_interval clean steps; AdamW scalars are computed in double and
+// rounded once to fp32.  Called by every thread of one workgroup: thread 0
+// takes the step decision, then thread h fills the scalars of hyper-group h.
+__device__ void finalize_block(double sumsq, double zeros, DevState *st, StepRec *sr, dopt_stats *out,
+                               const FinalizeArgs &a) {
+    __shared__ double s_t;
+    __shared__ int s_skip;
+    if (threadIdx.x == 0) {
+        const int found_inf = isfinite(sumsq) ? 0 : 1;
+        const double norm = sqrt(sumsq);
+        out->found_inf = found_inf;
+        out->skipped = found_inf;
+        out->reserved = 0;
+        out->sumsq = sumsq;
+        out->grad_norm = norm;
+        out->num_zeros = static_cast<uint64_t>(zeros);
+        out->loss_scale_used = st->scale;
+        sr->skip = found_inf;
+        sr->inv_scale = st->inv_scale;
+        if (st->kind == DOPT_SCALER_DYNAMIC) {
+            if (found_inf) {
+                st->growth_tracker = 0;
+                st->hysteresis_tracker -= 1;
+                if (st->hysteresis_tracker <= 0) st->scale = fmax(st->scale * st->backoff_factor, st->min_scale);
+            } else {
+                st->growth_tracker += 1;
+                if (st->growth_tracker == st->growth_interval) {
+                    st->growth_tracker = 0;
+                    st->hysteresis_tracker = st->hysteresis;
+                    st->scale = st->scale * st->growth_factor;
+                }
+            }
+            st->inv_scale = static_cast<float>(1.0 / st->scale);
+        }
+        out->loss_scale_next = st->scale;
+        double clip = 1.0;
+        int clip_on = 0;
+        if (!found_inf) {
+            st->t += 1;
+            if (a.max_norm > 0.0) {
+                clip = a.max_norm / (norm + 1e-6);
+                clip_on = clip < 1.0 ? 1 : 0;
+            }
+        }
+        out->clip_coef = clip;
+        out->clip_applied = clip_on;
+        sr->clip_on = clip_on;
+        sr->clip = clip_on ? static_cast<float>(clip) : 0.0f;
+        out->step_count = st->t;
+        s_t = static_cast<double>(st->t);
+        s_skip = found_inf;
+    }
+    __syncthreads();
+    const int h = threadIdx.x;
+    if (!s_skip && h < a.nh) {
+        const dopt_hparams &hp = a.hp[h];
+        sr->decay[h] = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+        sr->beta1[h] = static_cast<float>(hp.beta1);
+        sr->omb1[h] = static_cast<float>(1.0 - hp.beta1);
+        sr->beta2[h] = static_cast<float>(hp.beta2);
+        sr->omb2[h] = static_cast<float>(1.0 - hp.beta2);
+        sr->eps[h] = static_cast<float>(hp.eps);
+        sr->step_size[h] = static_cast<float>(hp.lr / (1.0 - pow(hp.beta1, s_t)));
+        sr->sqrt_bc2[h] = static_cast<float>(sqrt(1.0 - pow(hp.beta2, s_t)));
+    }
+}
+
+__global__ void __launch_bounds__(64) k_finalize(const Record *rec, DevState *st, StepRec *sr, dopt_stats *out,
+                                                 FinalizeArgs a) {
+    finalize_block(rec->sumsq, rec->zeros, st, sr, out, a);
+}
+
 // ---- pass 1: unscale, sum of squares, zero count -----------------------------
 //
 // [DO] "三层继承体系", second layer (grads to fp32 + unscale + inf/NaN) and
@@ -166,6 +260,10 @@ __device__ __forceinline__ int owner_hgroup(const SegDesc *__restrict__ segs, in
 // g*g is exact in double, so the double sum of squares is finite exactly when
 // every g is finite (its largest possible value, 2^64 * (2^128)^2, is far
 // below the double range): the inf/NaN flag is read off the final sum.
+//
+// Each workgroup writes one partial (double sum of squares, integer zero
+// count); k_finish then adds all partials in index order -- the same order
+// every run, whatever the device -- so the result is deterministic.
 
 __device__ __forceinline__ void block_sum_store(double acc, unsigned long long z, Partial *__restrict__ dst) {
 #pragma unroll
@@ -201,130 +299,101 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
     const float inv = st->inv_scale;
     double acc = 0.0;
     uint32_t zeros = 0;
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        const TileDesc td = tiles[t];
-        const int32_t cnt = td.seg_count & kTileCountMask;
-        if (cnt == 0) continue;
-        const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
-        float g[kVec];
-        Elem<GD>::load8(grad, i0, g);
-        if (td.seg_count & kTileFull) {
+    const int64_t G = gridDim.x;
+    for (int64_t t0 = blockIdx.x; t0 < n_tiles; t0 += kStatsUnroll * G) {
+        TileDesc td[kStatsUnroll];
+        float g[kStatsUnroll][kVec];
 #pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                const float x = g[j] * inv;
-                const double xd = static_cast<double>(x);
-                acc = fma(xd, xd, acc);
-                zeros += (x == 0.0f) ? 1u : 0u;
-            }
-        } else {
+        for (int u = 0; u < kStatsUnroll; ++u) {
+            const int64_t t = t0 + u * G;
+            td[u] = t < n_tiles ? tiles[t] : TileDesc{0, 0};
+            if (td[u].seg_count & kTileCountMask) Elem<GD>::load8(grad, t * kTile + int64_t(threadIdx.x) * kVec, g[u]);
+        }
 #pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                if (owner_hgroup(segs, td.seg_first, cnt, i0 + j) < 0) continue;
-                const float x = g[j] * inv;
-                const double xd = static_cast<double>(x);
-                acc = fma(xd, xd, acc);
-                zeros += (x == 0.0f) ? 1u : 0u;
+        for (int u = 0; u < kStatsUnroll; ++u) {
+            const int32_t cnt = td[u].seg_count & kTileCountMask;
+            if (cnt == 0) continue;
+            if (td[u].seg_count & kTileFull) {
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) {
+                    const float x = g[u][j] * inv;
+                    const double xd = static_cast<double>(x);
+                    acc = fma(xd, xd, acc);
+                    zeros += (x == 0.0f) ? 1u : 0u;
+                }
+            } else {
+                const int64_t i0 = (t0 + u * G) * kTile + int64_t(threadIdx.x) * kVec;
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) {
+                    if (owner_hgroup(segs, td[u].seg_first, cnt, i0 + j) < 0) continue;
+                    const float x = g[u][j] * inv;
+                    const double xd = static_cast<double>(x);
+                    acc = fma(xd, xd, acc);
+                    zeros += (x == 0.0f) ? 1u : 0u;
+                }
             }
         }
     }
     block_sum_store(acc, zeros, out + blockIdx.x);
 }
 
-// Fixed-order reduction of the per-workgroup partials into the record.
-__global__ void __launch_bounds__(kBlock) k_reduce(const Partial *__restrict__ part, int32_t n, Record *__restrict__ rec) {
-    __shared__ double s_acc[kBlock];
-    __shared__ unsigned long long s_z[kBlock];
+// One workgroup: the fixed-order sum of all partials into the record, and in
+// the fused form the finalize of the step.  Thread i adds partials i, i+256,
+// ... in order (loads issued together, kFinishBatch at a time), each wave
+// folds its 64 lanes with a fixed butterfly, and thread 0 adds the four wave
+// sums in order.
+constexpr int kFinishBatch = 4;
+
+template <bool FINALIZE>
+__global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ part, int32_t n,
+                                                  Record *__restrict__ rec, DevState *__restrict__ st,
+                                                  StepRec *__restrict__ sr, dopt_stats *__restrict__ out,
+                                                  FinalizeArgs fa) {
     double a = 0.0;
     unsigned long long z = 0;
-    for (int32_t i = threadIdx.x; i < n; i += kBlock) {
-        a += part[i].sumsq;
-        z += part[i].zeros;
+    for (int32_t i0 = threadIdx.x; i0 < n; i0 += kFinishBatch * kBlock) {
+        Partial q[kFinishBatch];
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+            const int32_t i = i0 + j * kBlock;
+            q[j] = i < n ? part[i] : Partial{0.0, 0ull};
+        }
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+            a += q[j].sumsq;
+            z += q[j].zeros;
+        }
     }
-    s_acc[threadIdx.x] = a;
-    s_z[threadIdx.x] = z;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        z += __shfl_xor(z, off, 64);
+    }
+    __shared__ double s_acc[kBlock / 64];
+    __shared__ unsigned long long s_z[kBlock / 64];
+    __shared__ double s_tot[2];
+    if ((threadIdx.x & 63) == 0) {
+        s_acc[threadIdx.x >> 6] = a;
+        s_z[threadIdx.x >> 6] = z;
+    }
     __syncthreads();
-    for (int w = kBlock / 2; w > 0; w >>= 1) {
-        if (static_cast<int>(threadIdx.x) < w) {
-            s_acc[threadIdx.x] += s_acc[threadIdx.x + w];
-            s_z[threadIdx.x] += s_z[threadIdx.x + w];
-        }
-        __syncthreads();
-    }
     if (threadIdx.x == 0) {
-        rec->sumsq = s_acc[0];
-        rec->zeros = static_cast<double>(s_z[0]);
-    }
-}
-
-// ---- finalize: skip, norm, clip, loss scale, step count, AdamW scalars ------
-//
-// [DO] "三层继承体系": an overflow skips the inner step; clipping uses the
-// global norm.  [DS] §3 config: dynamic loss scale starting at 2^16.  Clip
-// coefficient max_norm / (norm + 1e-6), applied when below 1; the dynamic
-// scale backs off (after `hysteresis` overflows) and grows every
-// growth_interval clean steps; AdamW scalars are computed in double and
-// rounded once to fp32.
-__global__ void k_finalize(const Record *__restrict__ rec, DevState *__restrict__ st, StepRec *__restrict__ sr,
-                           dopt_stats *__restrict__ out, FinalizeArgs a) {
-    if (threadIdx.x != 0) return;
-    const double sumsq = rec->sumsq;
-    const int found_inf = isfinite(sumsq) ? 0 : 1;
-    dopt_stats o;
-    memset(&o, 0, sizeof o);
-    StepRec r;
-    memset(&r, 0, sizeof r);
-    o.found_inf = found_inf;
-    o.skipped = found_inf;
-    o.sumsq = sumsq;
-    o.grad_norm = sqrt(sumsq);
-    o.num_zeros = static_cast<uint64_t>(rec->zeros);
-    o.loss_scale_used = st->scale;
-    r.skip = found_inf;
-    r.inv_scale = st->inv_scale;
-    if (st->kind == DOPT_SCALER_DYNAMIC) {
-        if (found_inf) {
-            st->growth_tracker = 0;
-            st->hysteresis_tracker -= 1;
-            if (st->hysteresis_tracker <= 0) st->scale = fmax(st->scale * st->backoff_factor, st->min_scale);
-        } else {
-            st->growth_tracker += 1;
-            if (st->growth_tracker == st->growth_interval) {
-                st->growth_tracker = 0;
-                st->hysteresis_tracker = st->hysteresis;
-                st->scale = st->scale * st->growth_factor;
-            }
+        double t = 0.0;
+        unsigned long long tz = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+            t += s_acc[w];
+            tz += s_z[w];
         }
-        st->inv_scale = static_cast<float>(1.0 / st->scale);
+        rec->sumsq = t;
+        rec->zeros = static_cast<double>(tz);
+        s_tot[0] = t;
+        s_tot[1] = static_cast<double>(tz);
     }
-    o.loss_scale_next = st->scale;
-    o.clip_coef = 1.0;
-    if (!found_inf) {
-        st->t += 1;
-        if (a.max_norm > 0.0) {
-            const double c = a.max_norm / (o.grad_norm + 1e-6);
-            o.clip_coef = c;
-            if (c < 1.0) {
-                o.clip_applied = 1;
-                r.clip_on = 1;
-                r.clip = static_cast<float>(c);
-            }
-        }
-        const double tt = static_cast<double>(st->t);
-        for (int h = 0; h < a.nh; ++h) {
-            const dopt_hparams &hp = a.hp[h];
-            r.decay[h] = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
-            r.beta1[h] = static_cast<float>(hp.beta1);
-            r.omb1[h] = static_cast<float>(1.0 - hp.beta1);
-            r.beta2[h] = static_cast<float>(hp.beta2);
-            r.omb2[h] = static_cast<float>(1.0 - hp.beta2);
-            r.eps[h] = static_cast<float>(hp.eps);
-            r.step_size[h] = static_cast<float>(hp.lr / (1.0 - pow(hp.beta1, tt)));
-            r.sqrt_bc2[h] = static_cast<float>(sqrt(1.0 - pow(hp.beta2, tt)));
-        }
+    if (FINALIZE) {
+        __syncthreads();
+        finalize_block(s_tot[0], s_tot[1], st, sr, out, fa);
     }
-    o.step_count = st->t;
-    *sr = r;
-    *out = o;
 }
 
 // ---- pass 2: clip + AdamW + bias correction + write-back --------------------
@@ -424,8 +493,7 @@ __global__ void __launch_bounds__(kBlock) k_init(const void *__restrict__ param,
     }
 }
 
-__global__ void k_init_state(DevState *__restrict__ st, StepRec *__restrict__ sr, dopt_stats *__restrict__ stats,
-                             Record *__restrict__ rec, InitArgs a) {
+__global__ void k_init_state(DevState *st, StepRec *sr, dopt_stats *stats, Record *rec, InitArgs a) {
     if (threadIdx.x != 0) return;
     *st = a.st;
     StepRec r;
@@ -486,6 +554,61 @@ static void launch_apply_gd(int gd, dim3 grid, hipStream_t s, const dopt_buffer_
                                                     n_tiles, rec);
         break;
     }
+}
+
+static int build_finalize_args(const dopt_layout *L, const dopt_hparams *hp, int32_t n_hgroups, double max_grad_norm,
+                               FinalizeArgs &a) {
+    if (!hp) return fail(DOPT_ERR_INVALID, "null hparams");
+    if (n_hgroups < L->max_hgroup + 1 || n_hgroups > DOPT_MAX_HGROUPS)
+        return fail(DOPT_ERR_INVALID, "n_hgroups must cover every hgroup of the params (<= DOPT_MAX_HGROUPS)");
+    std::memset(&a, 0, sizeof a);
+    for (int32_t h = 0; h < n_hgroups; ++h) {
+        const dopt_hparams &x = hp[h];
+        if (!(x.lr >= 0.0) || !(x.beta1 >= 0.0 && x.beta1 < 1.0) || !(x.beta2 >= 0.0 && x.beta2 < 1.0) ||
+            !(x.eps > 0.0) || !(x.weight_decay >= 0.0))
+            return fail(DOPT_ERR_INVALID,
+                        "hparams " + std::to_string(h) + ": need lr >= 0, 0 <= betas < 1, eps > 0, wd >= 0");
+        a.hp[h] = x;
+    }
+    a.nh = n_hgroups;
+    a.max_norm = max_grad_norm;
+    return DOPT_OK;
+}
+
+// Pass 1 over every buffer, then k_finish (reduction, and the finalize when
+// FINALIZE is set).
+template <bool FINALIZE>
+static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream,
+                        const FinalizeArgs &fa) {
+    const DevState *st = reinterpret_cast<const DevState *>(ws_ptr(ws, kWsState));
+    Partial *part = reinterpret_cast<Partial *>(ws_ptr(ws, kWsPartials));
+    for (size_t k = 0; k < L->buffers.size(); ++k) {
+        const Buffer &B = L->buffers[k];
+        const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
+        const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
+        const int64_t n_tiles = B.arena_numel / kTile;
+        const dim3 grid(B.stats_grid);
+        Partial *out = part + B.partial_base;
+        switch (B.gd) {
+        case DOPT_BF16:
+            k_stats<DOPT_BF16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            break;
+        case DOPT_F16:
+            k_stats<DOPT_F16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            break;
+        default:
+            k_stats<DOPT_F32><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            break;
+        }
+        int rc = check_launch("launch k_stats");
+        if (rc) return rc;
+    }
+    k_finish<FINALIZE><<<1, kBlock, 0, stream>>>(part, L->total_partials,
+                                                 reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
+                                                 reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
+                                                 reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
+                                                 reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), fa);
+    return check_launch("launch k_finish");
 }
 
 }  // namespace dopt
@@ -554,53 +677,31 @@ int dopt_init_state(const dopt_layout *L, const dopt_buffer_tensors *bufs, const
 int dopt_step_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream) {
     int rc = check_bufs(L, bufs, ws, true);
     if (rc != DOPT_OK) return rc;
-    const DevState *st = reinterpret_cast<const DevState *>(ws_ptr(ws, kWsState));
-    Partial *part = reinterpret_cast<Partial *>(ws_ptr(ws, kWsPartials));
-    for (size_t k = 0; k < L->buffers.size(); ++k) {
-        const Buffer &B = L->buffers[k];
-        const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
-        const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
-        const int64_t n_tiles = B.arena_numel / kTile;
-        const dim3 grid(B.stats_grid);
-        Partial *out = part + B.partial_base;
-        switch (B.gd) {
-        case DOPT_BF16:
-            k_stats<DOPT_BF16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
-            break;
-        case DOPT_F16:
-            k_stats<DOPT_F16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
-            break;
-        default:
-            k_stats<DOPT_F32><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
-            break;
-        }
-        if ((rc = check_launch("launch k_stats"))) return rc;
-    }
-    k_reduce<<<1, kBlock, 0, stream>>>(part, L->total_partials, reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)));
-    return check_launch("launch k_reduce");
+    FinalizeArgs none;
+    std::memset(&none, 0, sizeof none);
+    return launch_stats<false>(L, bufs, ws, stream, none);
 }
 
 int dopt_step_finalize(const dopt_layout *L, const dopt_hparams *hp, int32_t n_hgroups, double max_grad_norm,
                        void *ws, hipStream_t stream) {
-    if (!L || !hp || !ws) return fail(DOPT_ERR_INVALID, "null layout, hparams or workspace");
-    if (n_hgroups < L->max_hgroup + 1 || n_hgroups > DOPT_MAX_HGROUPS)
-        return fail(DOPT_ERR_INVALID, "n_hgroups must cover every hgroup of the params (<= DOPT_MAX_HGROUPS)");
+    if (!L || !ws) return fail(DOPT_ERR_INVALID, "null layout or workspace");
     FinalizeArgs a;
-    std::memset(&a, 0, sizeof a);
-    for (int32_t h = 0; h < n_hgroups; ++h) {
-        const dopt_hparams &x = hp[h];
-        if (!(x.lr >= 0.0) || !(x.beta1 >= 0.0 && x.beta1 < 1.0) || !(x.beta2 >= 0.0 && x.beta2 < 1.0) ||
-            !(x.eps > 0.0) || !(x.weight_decay >= 0.0))
-            return fail(DOPT_ERR_INVALID, "hparams " + std::to_string(h) + ": need lr >= 0, 0 <= betas < 1, eps > 0, wd >= 0");
-        a.hp[h] = x;
-    }
-    a.nh = n_hgroups;
-    a.max_norm = max_grad_norm;
+    int rc = build_finalize_args(L, hp, n_hgroups, max_grad_norm, a);
+    if (rc) return rc;
     k_finalize<<<1, 64, 0, stream>>>(reinterpret_cast<const Record *>(ws_ptr(ws, kWsRecord)),
                                      reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
                                      reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
                                      reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), a);
     return check_launch("launch k_finalize");
+}
+
+int dopt_step_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, const dopt_hparams *hp,
+                      int32_t n_hgroups, double max_grad_norm, void *ws, hipStream_t stream) {
+    int rc = check_bufs(L, bufs, ws, true);
+    if (rc != DOPT_OK) return rc;
+    FinalizeArgs a;
+    if ((rc = build_finalize_args(L, hp, n_hgroups, max_grad_norm, a))) return rc;
+    return launch_stats<true>(L, bufs, ws, stream, a);
 }
 
 int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream) {
@@ -640,9 +741,8 @@ int dopt_read_stats(const dopt_layout *L, const void *ws, hipStream_t stream, do
 
 int dopt_step(const dopt_layout *L, const dopt_buffer_tensors *bufs, const dopt_hparams *hp, int32_t n_hgroups,
               double max_grad_norm, void *ws, hipStream_t stream, dopt_stats *out) {
-    int rc = dopt_step_stats(L, bufs, ws, stream);
+    int rc = dopt_step_prepare(L, bufs, hp, n_hgroups, max_grad_norm, ws, stream);
     if (rc) return rc;
-    if ((rc = dopt_step_finalize(L, hp, n_hgroups, max_grad_norm, ws, stream))) return rc;
     if ((rc = dopt_step_apply(L, bufs, ws, stream))) return rc;
     if (out) return dopt_read_stats(L, ws, stream, out);
     return DOPT_OK;

@@ -184,10 +184,14 @@ class DeviceRun:
         sc = self.D.scaler_cfg(c.dynamic, c.initial_scale)
         self.D.dopt_init_state(self.L, self.A.bufs, sc, self.A.workspace, self.stream)
 
-    def step(self, host_grads: List[torch.Tensor], split: bool = False) -> dict:
+    def step(self, host_grads: List[torch.Tensor], split: bool = False, halves: bool = False) -> dict:
         for k, t in enumerate(host_grads):
             self.A.bufs[k]["grad"].copy_(t)
         c = self.case
+        if halves:
+            self.D.dopt_step_prepare(self.L, self.A.bufs, c.hparams, c.max_norm, self.A.workspace, self.stream)
+            self.D.dopt_step_apply(self.L, self.A.bufs, self.A.workspace, self.stream)
+            return self.D.dopt_read_stats(self.L, self.A.workspace, self.stream)
         if split:
             self.D.dopt_step_stats(self.L, self.A.bufs, self.A.workspace, self.stream)
             self.D.dopt_step_finalize(self.L, c.hparams, c.max_norm, self.A.workspace, self.stream)
@@ -206,7 +210,7 @@ class DeviceRun:
 
 # ------------------------------------------------------------ full parity ---
 
-def run_full(case: Case, split_steps: Sequence[int] = ()) -> List[dict]:
+def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[int] = ()) -> List[dict]:
     """Every element compared after every step."""
     t0 = time.time()
     dev = DeviceRun(case)
@@ -237,7 +241,7 @@ def run_full(case: Case, split_steps: Sequence[int] = ()) -> List[dict]:
             b["grad"][:] = to_bits(g)
             grads.append(g)
         ref = orc.step(case.hparams, case.max_norm)
-        got = dev.step(grads, split=s in split_steps)
+        got = dev.step(grads, split=s in split_steps, halves=s in half_steps)
         check_stats(got, ref, s)
         rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": ref.norm}
         for k, b in enumerate(hp):
@@ -354,7 +358,7 @@ def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
     t = ctypes.c_int64(0)
     hpa = oracle.make_hparams(case.hparams)
     pos = inf_position(case, O) if case.inf_step else None
-    grads = [torch.empty(n, dtype=synth.torch_dtype(gd)) for (pd, gd, n) in infos]
+    grads = [torch.empty(n, dtype=synth.torch_dtype(gd), pin_memory=True) for (pd, gd, n) in infos]
     report = []
     for s in range(1, case.steps + 1):
         ts = time.time()

@@ -110,7 +110,7 @@ def test_clip_off_and_clip_active():
 
 def test_split_api_matches_one_call():
     params = [ParamSpec("a", 9000, "bf16", "bf16"), ParamSpec("n", 64, "f32", "f32")]
-    H.run_full(H.Case("split", params, 4, 2, steps=3), split_steps=(1, 3))
+    H.run_full(H.Case("split", params, 4, 2, steps=4), split_steps=(1, 3), half_steps=(2,))
 
 
 def test_deterministic():
