@@ -17,11 +17,17 @@ constexpr int kVec = 8;
 constexpr int kTile = kBlock * kVec;
 static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile size");
 
-// Workgroups per launch (grid-stride over tiles).  Fixed per layout so that
-// the reduction order, and hence the sum of squares, does not depend on the
-// device it runs on.
+// Workgroups per launch.  Small windows get one workgroup per tile (pass 2)
+// or per kStatsUnroll tiles (pass 1), so no workgroup does more iterations
+// than another; large ones a fixed grid, grid-stride over the tiles.  The
+// grid is a function of the layout only, so the reduction order, and hence
+// the sum of squares, does not depend on the device it runs on.
 constexpr int kStatsMaxBlocks = 1024;
 constexpr int kApplyMaxBlocks = 2048;
+constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which pass 2 uses one workgroup per tile
+// Grad windows above this size are streamed through pass 1 with
+// nontemporal loads (the MI355X last-level cache is 256 MB).
+constexpr int64_t kStreamingReadBytes = int64_t(192) << 20;
 // Tiles in flight per workgroup iteration of pass 1 (more bytes outstanding
 // per wave for a pass that only reads).
 constexpr int kStatsUnroll = 4;

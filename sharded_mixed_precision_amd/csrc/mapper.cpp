@@ -134,8 +134,11 @@ static void build_tiles(Buffer &B) {
         const bool full = cnt == 1 && B.segs[s].start <= lo && B.segs[s].end >= hi;
         B.tiles[t] = TileDesc{static_cast<int32_t>(s), cnt | (full ? kTileFull : 0)};
     }
-    B.stats_grid = static_cast<int32_t>(std::min<int64_t>(n_tiles, kStatsMaxBlocks));
-    B.apply_grid = static_cast<int32_t>(std::min<int64_t>(n_tiles, kApplyMaxBlocks));
+    const int64_t stats_one_pass = (n_tiles + kStatsUnroll - 1) / kStatsUnroll;
+    B.stats_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? stats_one_pass
+                                                                   : std::min<int64_t>(stats_one_pass, kStatsMaxBlocks));
+    B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
+                                                                   : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
 }
 
 static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg, dopt_layout &L) {

@@ -292,7 +292,7 @@ __device__ __forceinline__ void block_sum_store(double acc, unsigned long long z
     }
 }
 
-template <int GD>
+template <int GD, bool NT>
 __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad, const TileDesc *__restrict__ tiles,
                                                  const SegDesc *__restrict__ segs, int64_t n_tiles,
                                                  const DevState *__restrict__ st, Partial *__restrict__ out) {
@@ -306,8 +306,11 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
             const int64_t t = t0 + u * G;
-            td[u] = t < n_tiles ? tiles[t] : TileDesc{0, 0};
-            if (td[u].seg_count & kTileCountMask) Elem<GD>::load8(grad, t * kTile + int64_t(threadIdx.x) * kVec, g[u]);
+            // the data load does not wait for the tile descriptor: every tile
+            // below n_tiles is allocated arena memory
+            const bool in = t < n_tiles;
+            td[u] = in ? tiles[t] : TileDesc{0, 0};
+            if (in) Elem<GD>::template load8<NT>(grad, t * kTile + int64_t(threadIdx.x) * kVec, g[u]);
         }
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
@@ -441,15 +444,17 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
     const float clip = rec->clip;
     float *__restrict__ pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        // descriptor and data loads are issued together (arena memory is
+        // allocated for every tile); a tile with no param element goes
+        // through the per-element path and stores nothing
         const TileDesc td = tiles[t];
-        const int32_t cnt = td.seg_count & kTileCountMask;
-        if (cnt == 0) continue;
         const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
         float g[kVec], p[kVec], a[kVec], b[kVec];
         Elem<GD>::load8(grad, i0, g);
         load8f(pm, i0, p);
         load8f(m, i0, a);
         load8f(v, i0, b);
+        const int32_t cnt = td.seg_count & kTileCountMask;
         if (td.seg_count & kTileFull) {
             const Hp h = load_hp(rec, segs[td.seg_first].hgroup);
 #pragma unroll
@@ -589,15 +594,23 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
         const int64_t n_tiles = B.arena_numel / kTile;
         const dim3 grid(B.stats_grid);
         Partial *out = part + B.partial_base;
+        // Grad windows larger than the last-level cache are read with
+        // nontemporal loads (measured faster for pure streaming reads); smaller
+        // ones are read normally so that pass 2's second read can hit the cache.
+        const int64_t grad_bytes = B.arena_numel * (B.gd == DOPT_F32 ? 4 : 2);
+        const bool nt = grad_bytes > kStreamingReadBytes;
         switch (B.gd) {
         case DOPT_BF16:
-            k_stats<DOPT_BF16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            if (nt) k_stats<DOPT_BF16, true><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            else k_stats<DOPT_BF16, false><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
             break;
         case DOPT_F16:
-            k_stats<DOPT_F16><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            if (nt) k_stats<DOPT_F16, true><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            else k_stats<DOPT_F16, false><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
             break;
         default:
-            k_stats<DOPT_F32><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            if (nt) k_stats<DOPT_F32, true><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
+            else k_stats<DOPT_F32, false><<<grid, kBlock, 0, stream>>>(bufs[k].grad, tiles, segs, n_tiles, st, out);
             break;
         }
         int rc = check_launch("launch k_stats");
