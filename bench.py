@@ -119,6 +119,47 @@ def cpu_baseline(workload, seconds: float):
                       f"passes in {el:.1f}s, 1 thread"}
 
 
+def bench_reduce(args, w, L, A, bufs_c, hp_c, stream):
+    """The local half of a reduce-scatter with fp32 accumulation fused with
+    pass 1: dp_size bf16 chunks per window slot are summed in fp32 and written
+    to the grad arena, and the stats run on the stored value."""
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    N = w.dp_size
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    chunks = []
+    bytes_call = 0
+    for k, info in enumerate(A.info):
+        t = torch.empty(N * info["n"], dtype=torch.bfloat16, device="cuda")
+        t.normal_(0.0, w.grad_sigma, generator=gen)  # seeded synthetic chunks, drawn on the device
+        chunks.append(t)
+        bytes_call += info["window_numel"] * (N * 2 + ES[info["gd"]])
+    for _ in range(args.warmup):
+        D.dopt_reduce_prepare(L, bufs_c, chunks, "bf16", N, 1.0, hp_c, w.max_grad_norm, A.workspace, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        D.dopt_reduce_prepare(L, bufs_c, chunks, "bf16", N, 1.0, hp_c, w.max_grad_norm, A.workspace, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    gbps = bytes_call / (ms * 1e-3) / 1e9
+    E = sum(info["window_numel"] for info in A.info)
+    print(json.dumps({
+        "metric": "fused local fp32-accumulating reduce of dp_size bf16 chunks + pass 1, 1 MI355X",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank {w.dp_rank} of N={N}, {E} window slots, {N} bf16 chunks each",
+                   "bytes_per_call": bytes_call},
+        "roofline": {"bound": "hbm", "kernel": "k_reduce_stats (+ k_finish)", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_call": bytes_call},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +168,9 @@ def main():
     ap.add_argument("--workload", default="gpt2-small")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["step", "reduce"], default="step",
+                    help="step: the optimizer step (default); reduce: the fused local fp32-accumulating reduce of "
+                         "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the step: copy an fp32 buffer of this many MiB (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -178,6 +222,9 @@ def main():
     D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
     bufs_c = D.tensors(A.bufs)
     hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
+    if args.mode == "reduce":
+        bench_reduce(args, w, L, A, bufs_c, hp_c, stream)
+        return
 
     # dopt_step = dopt_step_prepare + dopt_step_apply; the two halves are
     # called here so that events can bracket the apply pass.

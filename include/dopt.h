@@ -79,13 +79,32 @@ typedef struct dopt_param_desc {
     int32_t hgroup;              /* optimizer param group, 0 <= hgroup < DOPT_MAX_HGROUPS */
 } dopt_param_desc;
 
+/*
+ * Sharding of one rank.  With num_instances = I > 1 the data-parallel domain
+ * of N ranks is split into I distributed-optimizer instances of N/I ranks
+ * each ([ZL] §5 "num_distributed_optimizer_instances：分层 ZeRO"; [DP] §3.1):
+ * buckets are padded and split across the N/I ranks of the rank's instance,
+ * and the rank's shard is taken at its rank inside the instance (the
+ * intra-instance rank of the reduce-scatter call in [DO] §7.1); the optimizer
+ * state is cut to 1/(N/I).  Reading: instance i holds the consecutive ranks
+ * [i*N/I, (i+1)*N/I), so the intra-instance rank is r mod (N/I).  The
+ * all-reduce across instances is the caller's.
+ */
 typedef struct dopt_shard_cfg {
     int32_t dp_size;             /* N >= 1 */
     int32_t dp_rank;             /* 0 <= r < N */
     int64_t bucket_size;         /* elements; <= 0: no size trigger (one bucket) */
-    int32_t pad_for_high_busbw;  /* nonzero: buckets padded to lcm(N,128,2^16) */
-    int32_t reserved;            /* 0 */
+    int32_t pad_for_high_busbw;  /* nonzero: buckets padded to lcm(N',128,2^16), N' the instance size */
+    int32_t num_instances;       /* I >= 1 dividing N (0 is taken as 1) */
 } dopt_shard_cfg;
+
+typedef struct dopt_sharding_info {
+    int32_t dp_size, dp_rank;
+    int32_t num_instances;
+    int32_t instance_size;       /* N / I: the ranks the optimizer state is split over */
+    int32_t instance_index;      /* r / (N / I) */
+    int32_t instance_rank;       /* r mod (N / I): the shard this rank owns */
+} dopt_sharding_info;
 
 typedef struct dopt_range { int64_t start, end; } dopt_range;
 
@@ -160,10 +179,13 @@ typedef struct dopt_param_info {
 } dopt_param_info;
 
 int32_t dopt_layout_num_buffers(const dopt_layout *layout);
+/* How this rank's shard was chosen (instances, intra-instance rank). */
+int dopt_layout_sharding(const dopt_layout *layout, dopt_sharding_info *out);
 int dopt_layout_buffer(const dopt_layout *layout, int32_t k, dopt_buffer_info *out);
 int dopt_layout_bucket(const dopt_layout *layout, int32_t k, int32_t b, dopt_bucket_info *out);
-/* Window of rank `rank` (any rank, not only this one) in bucket b of buffer k,
- * buffer coordinates ([DO] "Bucket 级别的均等切分": all ranks' ranges). */
+/* Window of rank `rank` of the instance (any rank, not only this one; 0 <=
+ * rank < instance size) in bucket b of buffer k, buffer coordinates ([DO]
+ * "Bucket 级别的均等切分": all ranks' ranges). */
 int dopt_layout_rank_window(const dopt_layout *layout, int32_t k, int32_t b, int32_t rank, dopt_range *out);
 int dopt_layout_param(const dopt_layout *layout, int64_t p, dopt_param_info *out);
 /* Model-order indices of the params of one group kind and hyper-group; writes
@@ -182,7 +204,8 @@ int64_t dopt_workspace_bytes(const dopt_layout *layout);
 
 /* ---- device arrays of one flat buffer (all in arena coordinates) ---- */
 typedef struct dopt_buffer_tensors {
-    const void *grad;   /* device, arena_numel x grad dtype: the rank's reduced grads; read only */
+    const void *grad;   /* device, arena_numel x grad dtype: the rank's reduced grads; read only
+                           (dopt_reduce_prepare writes it) */
     void *param;        /* device, arena_numel x param dtype: the rank's param windows; written back */
     float *master;      /* device, arena_numel fp32; NULL when the param dtype is fp32 */
     float *exp_avg;     /* device, arena_numel fp32: Adam m */
@@ -285,6 +308,34 @@ int dopt_step_finalize(const dopt_layout *layout, const dopt_hparams *hp, int32_
                        void *workspace, hipStream_t stream);
 int dopt_step_apply(const dopt_layout *layout, const dopt_buffer_tensors *bufs, void *workspace,
                     hipStream_t stream);
+
+/*
+ * dopt_reduce_prepare -- the local half of a reduce-scatter with fp32
+ * accumulation fused with pass 1 ([DP] §3.2,
+ * reduce_scatter_with_fp32_accumulation: low precision on the wire, fp32
+ * accumulation on the receiving rank, via all-to-all).  After the all-to-all
+ * this rank holds one chunk of its windows from every rank of the group;
+ * per arena slot
+ *     g = (((0 + c_0) + c_1) + ... + c_{N-1}) * scale      (fp32, chunk order)
+ * is written to bufs[k].grad in the buffer's grad dtype (round to nearest
+ * even for 16-bit), and pass 1 (unscale, sum of squares, zero count) runs on
+ * the stored value in the same pass.  Reading: the pages fix neither the
+ * order of the sum nor where averaging happens; the sum runs in source-rank
+ * order and `scale` (e.g. 1/N for averaging, else 1) multiplies it once.
+ *
+ * chunks: host array of one device pointer per buffer; chunk j of buffer k
+ * is the arena_numel elements at chunks[k] + j * arena_numel, element type
+ * wire_dtype.  n_chunks must equal dp_size (one chunk per rank).  With hp
+ * non-NULL the step's finalize runs too (as in dopt_step_prepare; then call
+ * dopt_step_apply); with hp NULL only the grad-stats record is formed (as in
+ * dopt_step_stats; then dopt_step_finalize after the cross-rank sum).
+ * Errors: DOPT_ERR_INVALID (null or misaligned pointers, bad dtype,
+ * n_chunks != dp_size, num_instances > 1, which [DP] §3.2 rules out),
+ * DOPT_ERR_HIP.
+ */
+int dopt_reduce_prepare(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const void *const *chunks,
+                        int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp,
+                        int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream);
 
 /* Byte offset in the workspace of the grad-stats record: two doubles,
  * {sum of squares, zero count}; both are sums over ranks.  A non-finite sum

@@ -84,6 +84,7 @@ def _load():
     P, I32, I64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     sig = {
         "or_build": ([P(Param), I64, I32, I32, I64, I32, P(VP)], ctypes.c_int),
+        "or_build_instances": ([P(Param), I64, I32, I32, I32, I64, I32, P(VP)], ctypes.c_int),
         "or_free": ([VP], None),
         "or_error": ([], ctypes.c_char_p),
         "or_num_buffers": ([VP], I32),
@@ -101,6 +102,7 @@ def _load():
         "or_bf16_to_f32_n": ([VP, VP, I64], None),
         "or_f16_to_f32_n": ([VP, VP, I64], None),
         "or_init_state": ([VP, P(Arrays)], None),
+        "or_reduce_chunks": ([VP, I32, VP, I32, I32, I64, ctypes.c_float, I64, I64, VP], None),
         "or_grad_stats": ([VP, P(Arrays), ctypes.c_float, P(Stats)], None),
         "or_grad_stats_range": ([VP, I32, VP, ctypes.c_float, I64, I64, P(Stats)], None),
         "or_decide": ([P(Stats), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Scalars)], ctypes.c_int),
@@ -137,7 +139,8 @@ def _ptr(a):
 class Layout:
     """The oracle's shard layout for one rank (integer results)."""
 
-    def __init__(self, params: Sequence, dp_size: int, dp_rank: int, bucket_size: int = 0, pad_busbw: int = 0):
+    def __init__(self, params: Sequence, dp_size: int, dp_rank: int, bucket_size: int = 0, pad_busbw: int = 0,
+                 instances: int = 1):
         L = _load()
         n = len(params)
         arr = (Param * n)()
@@ -148,7 +151,10 @@ class Layout:
             arr[i].requires_new_bucket = int(getattr(p, "requires_new_bucket", 0))
             arr[i].hgroup = int(getattr(p, "hgroup", 0))
         h = ctypes.c_void_p()
-        rc = L.or_build(arr, n, dp_size, dp_rank, bucket_size, pad_busbw, ctypes.byref(h))
+        if instances == 1:
+            rc = L.or_build(arr, n, dp_size, dp_rank, bucket_size, pad_busbw, ctypes.byref(h))
+        else:
+            rc = L.or_build_instances(arr, n, dp_size, dp_rank, instances, bucket_size, pad_busbw, ctypes.byref(h))
         if rc != 0:
             raise OracleError(L.or_error().decode())
         self._h = h

@@ -238,6 +238,20 @@ int or_build(const or_param *params, int64_t n, int32_t dp_size, int32_t dp_rank
     return 0;
 }
 
+/*
+ * [ZL] §5 (num_distributed_optimizer_instances) and [DP] §3.1: the
+ * data-parallel domain of N ranks splits into I instances; the optimizer
+ * shards over the N/I ranks of one instance, at the rank's place inside it.
+ * Reading: instance i is the consecutive ranks [i*N/I, (i+1)*N/I).
+ */
+int or_build_instances(const or_param *params, int64_t n, int32_t dp_size, int32_t dp_rank, int32_t instances,
+                       int64_t bucket_size, int32_t pad_busbw, or_layout **out) {
+    if (instances < 1 || dp_size < 1 || dp_size % instances != 0) return fail("instances must divide dp_size");
+    if (dp_rank < 0 || dp_rank >= dp_size) return fail("invalid dp_size/dp_rank");
+    int32_t per = dp_size / instances;
+    return or_build(params, n, per, dp_rank % per, bucket_size, pad_busbw, out);
+}
+
 void or_free(or_layout *L) {
     if (!L) return;
     for (int32_t k = 0; k < L->n_buffers; ++k) {
@@ -418,6 +432,33 @@ static void store_param(void *base, int32_t dt, int64_t i, float x) {
     if (dt == OR_F32) ((float *)base)[i] = x;
     else if (dt == OR_BF16) ((uint16_t *)base)[i] = or_f32_to_bf16(x);
     else ((uint16_t *)base)[i] = or_f32_to_f16(x);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Local half of the fp32-accumulating reduce-scatter                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [DP] §3.2 (reduce_scatter_with_fp32_accumulation): the values travel in low
+ * precision and are accumulated in fp32 on the receiving rank.  For each
+ * window slot i of buffer k (slots [lo, hi) only):
+ *   acc = +0; acc = acc + chunk_j[i] for j = 0..n-1 (fp32, in chunk order);
+ *   acc = acc * scale; grad[i] = acc stored in the buffer's grad dtype
+ *   (round to nearest even for 16-bit).
+ * Chunk j starts stride elements after chunk j-1.  Readings: the pages fix
+ * neither the summation order nor the place of the averaging factor.
+ */
+void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t wire_dtype, int32_t n_chunks,
+                      int64_t stride, float scale, int64_t lo, int64_t hi, void *grad_out) {
+    f16_table_init();
+    const ob_buffer *B = &L->buf[k];
+    if (hi > B->window_numel) hi = B->window_numel;
+    for (int64_t i = lo; i < hi; ++i) {
+        float acc = 0.0f;
+        for (int32_t j = 0; j < n_chunks; ++j) acc = acc + load_f32(chunks, wire_dtype, (int64_t)j * stride + i);
+        acc = acc * scale;
+        store_param(grad_out, B->gd, i, acc);
+    }
 }
 
 /* ------------------------------------------------------------------------ */

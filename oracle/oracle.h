@@ -56,6 +56,9 @@ typedef struct or_layout or_layout;
  * Returns 0, or -1 with or_error() set. */
 int or_build(const or_param *params, int64_t n, int32_t dp_size, int32_t dp_rank,
              int64_t bucket_size, int32_t pad_busbw, or_layout **out);
+/* Same, with the data-parallel domain split into `instances` optimizer instances. */
+int or_build_instances(const or_param *params, int64_t n, int32_t dp_size, int32_t dp_rank, int32_t instances,
+                       int64_t bucket_size, int32_t pad_busbw, or_layout **out);
 void or_free(or_layout *L);
 const char *or_error(void);
 
@@ -82,6 +85,12 @@ void or_f32_to_bf16_n(const float *x, uint16_t *y, int64_t n);
 void or_f32_to_f16_n(const float *x, uint16_t *y, int64_t n);
 void or_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void or_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
+
+/* ---- local half of the fp32-accumulating reduce-scatter ---- */
+/* grad[i] = storage((sum over chunks in order, fp32, from +0) * scale) for
+ * window slots i in [lo, hi) of buffer k; chunk j at chunks + j*stride. */
+void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t wire_dtype, int32_t n_chunks,
+                      int64_t stride, float scale, int64_t lo, int64_t hi, void *grad_out);
 
 /* ---- the step ---- */
 typedef struct {

@@ -40,7 +40,13 @@ class dopt_param_desc(ctypes.Structure):
 
 class dopt_shard_cfg(ctypes.Structure):
     _fields_ = [("dp_size", ctypes.c_int32), ("dp_rank", ctypes.c_int32), ("bucket_size", ctypes.c_int64),
-                ("pad_for_high_busbw", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("pad_for_high_busbw", ctypes.c_int32), ("num_instances", ctypes.c_int32)]
+
+
+class dopt_sharding_info(ctypes.Structure):
+    _fields_ = [("dp_size", ctypes.c_int32), ("dp_rank", ctypes.c_int32), ("num_instances", ctypes.c_int32),
+                ("instance_size", ctypes.c_int32), ("instance_index", ctypes.c_int32),
+                ("instance_rank", ctypes.c_int32)]
 
 
 class dopt_range(ctypes.Structure):
@@ -105,6 +111,7 @@ def _load():
         "dopt_build_ranges": ([P(dopt_param_desc), I64, P(dopt_shard_cfg), P(VP)], ctypes.c_int),
         "dopt_layout_free": ([VP], None),
         "dopt_layout_num_buffers": ([VP], I32),
+        "dopt_layout_sharding": ([VP, P(dopt_sharding_info)], ctypes.c_int),
         "dopt_layout_buffer": ([VP, I32, P(dopt_buffer_info)], ctypes.c_int),
         "dopt_layout_bucket": ([VP, I32, I32, P(dopt_bucket_info)], ctypes.c_int),
         "dopt_layout_rank_window": ([VP, I32, I32, I32, P(dopt_range)], ctypes.c_int),
@@ -116,6 +123,8 @@ def _load():
         "dopt_step": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP, P(dopt_stats)], ctypes.c_int),
         "dopt_step_prepare": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_stats": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
+        "dopt_reduce_prepare": ([VP, P(dopt_buffer_tensors), P(VP), I32, I32, ctypes.c_float, P(dopt_hparams), I32, D,
+                                 VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
         "dopt_stats_record_offset": ([VP], I64),
@@ -130,10 +139,12 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", "dopt_layout_buffer",
+EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", "dopt_layout_sharding",
+            "dopt_layout_buffer",
             "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
             "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_prepare", "dopt_step_stats",
-            "dopt_step_finalize", "dopt_step_apply", "dopt_stats_record_offset", "dopt_read_stats",
+            "dopt_step_finalize", "dopt_step_apply", "dopt_reduce_prepare", "dopt_stats_record_offset",
+            "dopt_read_stats",
             "dopt_last_error")
 
 
@@ -184,6 +195,11 @@ class Layout:
     def num_buffers(self) -> int:
         return int(_lib.dopt_layout_num_buffers(self._h))
 
+    def sharding(self) -> Dict:
+        o = dopt_sharding_info()
+        _check(_lib.dopt_layout_sharding(self._h, ctypes.byref(o)))
+        return {name: getattr(o, name) for name, _ in o._fields_}
+
     def buffer(self, k: int) -> Dict:
         o = dopt_buffer_info()
         _check(_lib.dopt_layout_buffer(self._h, k, ctypes.byref(o)))
@@ -230,7 +246,7 @@ class Layout:
 
 
 def dopt_build_ranges(params: Sequence, dp_size: int, dp_rank: int, bucket_size: int = 0,
-                      pad_for_high_busbw: int = 0) -> Layout:
+                      pad_for_high_busbw: int = 0, num_instances: int = 1) -> Layout:
     """params: objects with numel, param_dtype, grad_dtype ('f32'|'bf16'|'f16'),
     optional requires_new_bucket and hgroup, in model order."""
     n = len(params)
@@ -241,7 +257,7 @@ def dopt_build_ranges(params: Sequence, dp_size: int, dp_rank: int, bucket_size:
         arr[i].grad_dtype = DTYPES[p.grad_dtype] if isinstance(p.grad_dtype, str) else p.grad_dtype
         arr[i].requires_new_bucket = int(getattr(p, "requires_new_bucket", 0))
         arr[i].hgroup = int(getattr(p, "hgroup", 0))
-    cfg = dopt_shard_cfg(dp_size, dp_rank, bucket_size, pad_for_high_busbw, 0)
+    cfg = dopt_shard_cfg(dp_size, dp_rank, bucket_size, pad_for_high_busbw, num_instances)
     h = ctypes.c_void_p()
     _check(_lib.dopt_build_ranges(arr, n, ctypes.byref(cfg), ctypes.byref(h)))
     return Layout(h, dp_size, dp_rank, n)
@@ -291,6 +307,21 @@ def dopt_step_prepare(layout: Layout, bufs, hparams, max_grad_norm: float, works
     t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
     hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
     _check(_lib.dopt_step_prepare(layout.handle, t, hp, len(hp), max_grad_norm, _addr(workspace), _stream(stream)))
+
+
+def dopt_reduce_prepare(layout: Layout, bufs, chunks: Sequence, wire_dtype: str, n_chunks: int, scale: float,
+                        hparams, max_grad_norm: float, workspace, stream=None):
+    """chunks: one device buffer per flat buffer holding n_chunks arenas back to back.
+    hparams None: stats only (finalize later with dopt_step_finalize)."""
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    ch = (ctypes.c_void_p * len(chunks))(*[_addr(c) for c in chunks])
+    if hparams is None:
+        hp, nh = None, 0
+    else:
+        hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
+        nh = len(hp)
+    _check(_lib.dopt_reduce_prepare(layout.handle, t, ch, DTYPES[wire_dtype], n_chunks, scale, hp, nh,
+                                    max_grad_norm, _addr(workspace), _stream(stream)))
 
 
 def dopt_step_stats(layout: Layout, bufs, workspace, stream=None):

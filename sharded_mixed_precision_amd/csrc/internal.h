@@ -86,7 +86,8 @@ int fail(int code, const std::string &msg);
 }  // namespace dopt
 
 struct dopt_layout {
-    int32_t N = 1, r = 0;
+    int32_t dp_size = 1, dp_rank = 0, num_instances = 1;
+    int32_t N = 1, r = 0;  // ranks the state is split over (the instance size) and this rank among them
     int32_t max_hgroup = 0;
     std::vector<dopt::Param> params;
     std::vector<dopt::Buffer> buffers;

@@ -142,8 +142,11 @@ static void build_tiles(Buffer &B) {
 }
 
 static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg, dopt_layout &L) {
-    L.N = cfg->dp_size;
-    L.r = cfg->dp_rank;
+    L.dp_size = cfg->dp_size;
+    L.dp_rank = cfg->dp_rank;
+    L.num_instances = cfg->num_instances > 0 ? cfg->num_instances : 1;
+    L.N = L.dp_size / L.num_instances;  // ranks of one distributed-optimizer instance
+    L.r = L.dp_rank % L.N;              // this rank inside its instance
     L.params.resize(static_cast<size_t>(n));
     for (int64_t i = 0; i < n; ++i) {
         const dopt_param_desc &d = params[i];
@@ -204,6 +207,8 @@ int dopt_build_ranges(const dopt_param_desc *params, int64_t n, const dopt_shard
     *out = nullptr;
     if (cfg->dp_size < 1 || cfg->dp_rank < 0 || cfg->dp_rank >= cfg->dp_size)
         return fail(DOPT_ERR_INVALID, "dp_rank must satisfy 0 <= dp_rank < dp_size");
+    if (cfg->num_instances < 0 || (cfg->num_instances > 0 && cfg->dp_size % cfg->num_instances != 0))
+        return fail(DOPT_ERR_INVALID, "num_instances must be >= 1 and divide dp_size");
     dopt_layout *L = new (std::nothrow) dopt_layout();
     if (!L) return fail(DOPT_ERR_NOMEM, "out of host memory");
     int rc;
@@ -223,6 +228,17 @@ int dopt_build_ranges(const dopt_param_desc *params, int64_t n, const dopt_shard
 void dopt_layout_free(dopt_layout *layout) { delete layout; }
 
 int32_t dopt_layout_num_buffers(const dopt_layout *L) { return L ? static_cast<int32_t>(L->buffers.size()) : 0; }
+
+int dopt_layout_sharding(const dopt_layout *L, dopt_sharding_info *out) {
+    if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");
+    out->dp_size = L->dp_size;
+    out->dp_rank = L->dp_rank;
+    out->num_instances = L->num_instances;
+    out->instance_size = L->N;
+    out->instance_index = L->dp_rank / L->N;
+    out->instance_rank = L->r;
+    return DOPT_OK;
+}
 
 int dopt_layout_buffer(const dopt_layout *L, int32_t k, dopt_buffer_info *out) {
     if (!L || !out) return fail(DOPT_ERR_INVALID, "null argument");

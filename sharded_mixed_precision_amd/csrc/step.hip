@@ -340,6 +340,70 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
     block_sum_store(acc, zeros, out + blockIdx.x);
 }
 
+// ---- fused local fp32 reduce + pass 1 -------------------------------------------
+//
+// [DP] §3.2 (reduce_scatter_with_fp32_accumulation): the N chunks this rank
+// received for each arena slot are added in fp32 in chunk order, starting
+// from +0, scaled once, stored in the grad dtype, and the stored value goes
+// through pass 1 exactly as in k_stats.  Chunk loads are issued kReduceBatch
+// at a time (the adds stay in chunk order); the chunks are read once, so
+// they are loaded nontemporally.
+constexpr int kReduceBatch = 4;
+
+template <int GD>
+__device__ __forceinline__ float stored_value(float x);
+template <>
+__device__ __forceinline__ float stored_value<DOPT_F32>(float x) { return x; }
+template <>
+__device__ __forceinline__ float stored_value<DOPT_BF16>(float x) { return __uint_as_float(Elem<DOPT_BF16>::bits(x) << 16); }
+template <>
+__device__ __forceinline__ float stored_value<DOPT_F16>(float x) { return Elem<DOPT_F16>::up(Elem<DOPT_F16>::bits(x)); }
+
+template <int WD, int GD>
+__global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict__ chunks, int64_t stride,
+                                                        int32_t n_chunks, float scale, void *__restrict__ grad,
+                                                        const TileDesc *__restrict__ tiles,
+                                                        const SegDesc *__restrict__ segs, int64_t n_tiles,
+                                                        const DevState *__restrict__ st, Partial *__restrict__ out) {
+    const float inv = st->inv_scale;
+    double acc = 0.0;
+    uint32_t zeros = 0;
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const TileDesc td = tiles[t];
+        const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
+        float s[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) s[j] = 0.0f;
+        for (int32_t c0 = 0; c0 < n_chunks; c0 += kReduceBatch) {
+            float x[kReduceBatch][kVec];
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b)
+                if (c0 + b < n_chunks) Elem<WD>::template load8<true>(chunks, int64_t(c0 + b) * stride + i0, x[b]);
+#pragma unroll
+            for (int b = 0; b < kReduceBatch; ++b) {
+                if (c0 + b >= n_chunks) break;
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[b][j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) s[j] = s[j] * scale;
+        Elem<GD>::store8(grad, i0, s);
+        const int32_t cnt = td.seg_count & kTileCountMask;
+        if (cnt == 0) continue;
+        const bool full = (td.seg_count & kTileFull) != 0;
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            if (!full && owner_hgroup(segs, td.seg_first, cnt, i0 + j) < 0) continue;
+            const float x = stored_value<GD>(s[j]) * inv;
+            const double xd = static_cast<double>(x);
+            acc = fma(xd, xd, acc);
+            zeros += (x == 0.0f) ? 1u : 0u;
+        }
+    }
+    block_sum_store(acc, zeros, out + blockIdx.x);
+}
+
 // One workgroup: the fixed-order sum of all partials into the record, and in
 // the fused form the finalize of the step.  Thread i adds partials i, i+256,
 // ... in order (loads issued together, kFinishBatch at a time), each wave
@@ -580,8 +644,19 @@ static int build_finalize_args(const dopt_layout *L, const dopt_hparams *hp, int
     return DOPT_OK;
 }
 
-// Pass 1 over every buffer, then k_finish (reduction, and the finalize when
-// FINALIZE is set).
+// The fixed-order reduction of all pass-1 partials, and the finalize when
+// FINALIZE is set.
+template <bool FINALIZE>
+static int launch_finish(const dopt_layout *L, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
+    k_finish<FINALIZE><<<1, kBlock, 0, stream>>>(reinterpret_cast<const Partial *>(ws_ptr(ws, kWsPartials)),
+                                                 L->total_partials, reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
+                                                 reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
+                                                 reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
+                                                 reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), fa);
+    return check_launch("launch k_finish");
+}
+
+// Pass 1 over every buffer, then k_finish.
 template <bool FINALIZE>
 static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream,
                         const FinalizeArgs &fa) {
@@ -616,12 +691,56 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
         int rc = check_launch("launch k_stats");
         if (rc) return rc;
     }
-    k_finish<FINALIZE><<<1, kBlock, 0, stream>>>(part, L->total_partials,
-                                                 reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
-                                                 reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
-                                                 reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
-                                                 reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), fa);
-    return check_launch("launch k_finish");
+    return launch_finish<FINALIZE>(L, ws, stream, fa);
+}
+
+template <int WD, int GD>
+static void launch_reduce_dt(dim3 grid, hipStream_t s, const void *chunks, int64_t stride, int32_t n, float scale,
+                             void *grad, const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles,
+                             const DevState *st, Partial *out) {
+    k_reduce_stats<WD, GD><<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+}
+
+template <int WD>
+static void launch_reduce_gd(int gd, dim3 grid, hipStream_t s, const void *chunks, int64_t stride, int32_t n,
+                             float scale, void *grad, const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles,
+                             const DevState *st, Partial *out) {
+    if (gd == DOPT_BF16)
+        launch_reduce_dt<WD, DOPT_BF16>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+    else if (gd == DOPT_F16)
+        launch_reduce_dt<WD, DOPT_F16>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+    else
+        launch_reduce_dt<WD, DOPT_F32>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+}
+
+// Fused local fp32 reduce + pass 1 over every buffer, then k_finish.
+template <bool FINALIZE>
+static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *const *chunks, int32_t wd,
+                         int32_t n_chunks, float scale, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
+    const DevState *st = reinterpret_cast<const DevState *>(ws_ptr(ws, kWsState));
+    Partial *part = reinterpret_cast<Partial *>(ws_ptr(ws, kWsPartials));
+    for (size_t k = 0; k < L->buffers.size(); ++k) {
+        const Buffer &B = L->buffers[k];
+        const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
+        const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
+        const int64_t n_tiles = B.arena_numel / kTile;
+        const dim3 grid(B.stats_grid);  // one partial per workgroup, as pass 1
+        Partial *out = part + B.partial_base;
+        // the grad arena is this entry point's output (read-only everywhere else)
+        void *grad_out = const_cast<void *>(bufs[k].grad);
+        if (wd == DOPT_BF16)
+            launch_reduce_gd<DOPT_BF16>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
+                                        tiles, segs, n_tiles, st, out);
+        else if (wd == DOPT_F16)
+            launch_reduce_gd<DOPT_F16>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
+                                       tiles, segs, n_tiles, st, out);
+        else
+            launch_reduce_gd<DOPT_F32>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
+                                       tiles, segs, n_tiles, st, out);
+        int rc = check_launch("launch k_reduce_stats");
+        if (rc) return rc;
+    }
+    return launch_finish<FINALIZE>(L, ws, stream, fa);
 }
 
 }  // namespace dopt
@@ -715,6 +834,29 @@ int dopt_step_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, con
     FinalizeArgs a;
     if ((rc = build_finalize_args(L, hp, n_hgroups, max_grad_norm, a))) return rc;
     return launch_stats<true>(L, bufs, ws, stream, a);
+}
+
+int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *const *chunks,
+                        int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp, int32_t n_hgroups,
+                        double max_grad_norm, void *ws, hipStream_t stream) {
+    int rc = check_bufs(L, bufs, ws, true);
+    if (rc != DOPT_OK) return rc;
+    if (L->num_instances != 1)
+        return fail(DOPT_ERR_INVALID, "the fp32-accumulating reduce does not support num_instances > 1");
+    if (wire_dtype != DOPT_F32 && wire_dtype != DOPT_BF16 && wire_dtype != DOPT_F16)
+        return fail(DOPT_ERR_INVALID, "bad wire dtype");
+    if (n_chunks != L->dp_size) return fail(DOPT_ERR_INVALID, "n_chunks must equal dp_size (one chunk per rank)");
+    if (!chunks) return fail(DOPT_ERR_INVALID, "null chunk array");
+    for (size_t k = 0; k < L->buffers.size(); ++k)
+        if (!chunks[k] || !aligned(chunks[k]))
+            return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": null or unaligned chunk pointer");
+    FinalizeArgs a;
+    std::memset(&a, 0, sizeof a);
+    if (hp) {
+        if ((rc = build_finalize_args(L, hp, n_hgroups, max_grad_norm, a))) return rc;
+        return launch_reduce<true>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
+    }
+    return launch_reduce<false>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
 }
 
 int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream) {

@@ -27,6 +27,7 @@ STREAM_WEIGHT = 1
 STREAM_GRAD = 2
 STREAM_ZERO_MASK = 3
 STREAM_INF_POS = 4
+STREAM_CHUNK = 5
 _BUFFER_STRIDE = 64  # stream offset between flat buffers
 
 
@@ -82,6 +83,11 @@ def weight_stream(buffer_index: int) -> int:
 
 def grad_stream(buffer_index: int) -> int:
     return buffer_stream(STREAM_GRAD, buffer_index)
+
+
+def chunk_stream(buffer_index: int) -> int:
+    """Stream of the received (pre-reduction) grad chunks of one buffer."""
+    return buffer_stream(STREAM_CHUNK, buffer_index)
 
 
 _TORCH_DTYPES = None

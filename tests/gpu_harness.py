@@ -57,6 +57,13 @@ class Case:
     hparams: List = field(default_factory=lambda: [(1e-3, 0.9, 0.999, 1e-8, 0.01)])
     max_norm: float = 1.0
     const_grad: Optional[float] = None  # all grads equal to this value
+    instances: int = 1
+    # grads produced by the fp32-accumulating local reduce of `chunks` received
+    # chunks in the `wire` dtype (0: grads drawn directly)
+    chunks: int = 0
+    wire: str = "bf16"
+    reduce_scale: float = 1.0
+    reduce_split: bool = False
 
     def scale_at(self, step: int) -> float:
         if not self.dynamic:
@@ -87,6 +94,12 @@ def host_grads(case: Case, k: int, dt: str, n: int, step: int, out=None):
         return t
     return synth.fill_normal(dt, n, case.seed, synth.grad_stream(k), step, case.grad_sigma,
                              scale=case.scale_at(step), zero_frac=case.zero_frac, out=out)
+
+
+def host_chunks(case: Case, k: int, n: int, step: int, out=None):
+    """case.chunks received chunks of an n-slot arena, back to back, in the wire dtype."""
+    return synth.fill_normal(case.wire, case.chunks * n, case.seed, synth.chunk_stream(k), step, case.grad_sigma,
+                             zero_frac=case.zero_frac, out=out)
 
 
 def inf_position(case: Case, O: oracle.Layout):
@@ -172,7 +185,8 @@ class DeviceRun:
         D = _dopt()
         from sharded_mixed_precision_amd.arena import DeviceArenas
         self.D = D
-        self.L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw)
+        self.L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw,
+                                     case.instances)
         self.A = DeviceArenas(self.L)
         self.stream = torch.cuda.current_stream()
         self.case = case
@@ -199,6 +213,23 @@ class DeviceRun:
             return self.D.dopt_read_stats(self.L, self.A.workspace, self.stream)
         return self.D.dopt_step(self.L, self.A.bufs, c.hparams, c.max_norm, self.A.workspace, self.stream)
 
+    def step_reduce(self, host_chunks: List[torch.Tensor]) -> dict:
+        """The step with its grads formed on the device by dopt_reduce_prepare."""
+        c = self.case
+        if not hasattr(self, "dev_chunks"):
+            self.dev_chunks = [torch.empty(t.numel(), dtype=t.dtype, device="cuda") for t in host_chunks]
+        for d, t in zip(self.dev_chunks, host_chunks):
+            d.copy_(t)
+        if c.reduce_split:
+            self.D.dopt_reduce_prepare(self.L, self.A.bufs, self.dev_chunks, c.wire, c.chunks, c.reduce_scale, None,
+                                       c.max_norm, self.A.workspace, self.stream)
+            self.D.dopt_step_finalize(self.L, c.hparams, c.max_norm, self.A.workspace, self.stream)
+        else:
+            self.D.dopt_reduce_prepare(self.L, self.A.bufs, self.dev_chunks, c.wire, c.chunks, c.reduce_scale,
+                                       c.hparams, c.max_norm, self.A.workspace, self.stream)
+        self.D.dopt_step_apply(self.L, self.A.bufs, self.A.workspace, self.stream)
+        return self.D.dopt_read_stats(self.L, self.A.workspace, self.stream)
+
     def host(self, k: int, key: str) -> np.ndarray:
         t = self.A.bufs[k][key]
         return to_bits(t.cpu())
@@ -215,7 +246,8 @@ def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[i
     t0 = time.time()
     dev = DeviceRun(case)
     arena = [dev.L.buffer(k)["arena_numel"] for k in range(dev.L.num_buffers)]
-    orc = OracleRun(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, arena_numel=arena)
+    orc = OracleRun(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, arena_numel=arena,
+                    instances=case.instances)
     for k in range(orc.nb):
         w = orc.L.buffer(k)["window_numel"]
         assert arena[k] == -(-max(w, 1) // dev.D.DOPT_ARENA_ALIGN) * dev.D.DOPT_ARENA_ALIGN
@@ -233,17 +265,31 @@ def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[i
     pos = inf_position(case, orc.L) if case.inf_step else None
     report = []
     for s in range(1, case.steps + 1):
-        grads = []
+        grads, chunks = [], []
         for k, b in enumerate(hp):
+            if case.chunks:
+                ch = host_chunks(case, k, b["n"], s)
+                chunks.append(ch)
+                oracle.lib().or_reduce_chunks(orc.L.handle, k, ch.data_ptr(), oracle.DTYPES[case.wire], case.chunks,
+                                              b["n"], case.reduce_scale, 0, b["n"], b["grad"].ctypes.data)
+                continue
             g = host_grads(case, k, b["gd"], b["n"], s)
             if pos is not None and s == case.inf_step and pos[0] == k:
                 g[pos[1]] = case.inf_value
             b["grad"][:] = to_bits(g)
             grads.append(g)
         ref = orc.step(case.hparams, case.max_norm)
-        got = dev.step(grads, split=s in split_steps, halves=s in half_steps)
+        if case.chunks:
+            got = dev.step_reduce(chunks)
+        else:
+            got = dev.step(grads, split=s in split_steps, halves=s in half_steps)
         check_stats(got, ref, s)
         rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": ref.norm}
+        if case.chunks:  # the reduced grad window, every slot, bit for bit
+            for k, b in enumerate(hp):
+                w = orc.L.buffer(k)["window_numel"]
+                gdev = dev.host(k, "grad")[:w]
+                assert np.array_equal(gdev.view(np.uint8), b["grad"][:w].view(np.uint8)), f"step {s}: reduced grad[{k}]"
         for k, b in enumerate(hp):
             m = masks[k]
             if b["pd"] != "f32":
@@ -314,13 +360,29 @@ def oracle_stats_parallel(O: oracle.Layout, grads: List[torch.Tensor], inv_scale
     return out
 
 
+def oracle_reduce_parallel(O: oracle.Layout, k: int, chunks: torch.Tensor, wire: str, n_chunks: int, stride: int,
+                           scale: float, grad_out: torch.Tensor, workers: int = 16, chunk: int = 1 << 24):
+    """The oracle's local fp32 reduce over disjoint slot ranges on host threads
+    (each range one plain single-threaded oracle call; every slot is computed
+    exactly once, so the result does not depend on the split)."""
+    lib = oracle.lib()
+    n = grad_out.numel()
+
+    def run(lo):
+        lib.or_reduce_chunks(O.handle, k, chunks.data_ptr(), oracle.DTYPES[wire], n_chunks, stride, scale, lo,
+                             min(lo + chunk, n), grad_out.data_ptr())
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(run, range(0, n, chunk)))
+
+
 def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
     """Full-size run on the device; the oracle computes the exact per-step
     stats over all shard elements and the trajectories of sampled elements."""
     t0 = time.time()
     lib = oracle.lib()
     dev = DeviceRun(case)
-    O = oracle.Layout(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw)
+    O = oracle.Layout(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, case.instances)
     nb = O.num_buffers
     infos = []
     for k in range(nb):
@@ -359,10 +421,16 @@ def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
     hpa = oracle.make_hparams(case.hparams)
     pos = inf_position(case, O) if case.inf_step else None
     grads = [torch.empty(n, dtype=synth.torch_dtype(gd), pin_memory=True) for (pd, gd, n) in infos]
+    chunks = [torch.empty(case.chunks * n, dtype=synth.torch_dtype(case.wire), pin_memory=True)
+              for (pd, gd, n) in infos] if case.chunks else None
     report = []
     for s in range(1, case.steps + 1):
         ts = time.time()
         for k, (pd, gd, n) in enumerate(infos):
+            if case.chunks:
+                host_chunks(case, k, n, s, out=chunks[k])
+                oracle_reduce_parallel(O, k, chunks[k], case.wire, case.chunks, n, case.reduce_scale, grads[k])
+                continue
             host_grads(case, k, gd, n, s, out=grads[k])
             if pos is not None and s == case.inf_step and pos[0] == k:
                 grads[k][pos[1]] = case.inf_value
@@ -377,7 +445,12 @@ def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
                                gs.ctypes.data, st_master[k].ctypes.data, st_m[k].ctypes.data, st_v[k].ctypes.data,
                                st_param[k].ctypes.data, ctypes.byref(sc))
         to = time.time()
-        got = dev.step(grads)
+        got = dev.step_reduce(chunks) if case.chunks else dev.step(grads)
+        if case.chunks:  # sampled slots of the reduced grad window, bit for bit
+            for k in range(nb):
+                gd_dev = dev.gather(k, "grad", dev_idx[k])
+                assert np.array_equal(gd_dev.view(np.uint8), to_bits(grads[k])[samples[k]].view(np.uint8)), \
+                    f"step {s}: reduced grad[{k}] samples"
         check_stats(got, st, s)
         rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": st.norm, "skipped": got["skipped"]}
         for k, (pd, gd, n) in enumerate(infos):

@@ -36,8 +36,8 @@ def as_f32(a: np.ndarray, dt: str) -> np.ndarray:
 class OracleRun:
     """Holds a layout, its arena arrays and the scaler / step state."""
 
-    def __init__(self, params, dp_size, dp_rank, bucket_size=0, pad_busbw=0, arena_numel=None):
-        self.L = oracle.Layout(params, dp_size, dp_rank, bucket_size, pad_busbw)
+    def __init__(self, params, dp_size, dp_rank, bucket_size=0, pad_busbw=0, arena_numel=None, instances=1):
+        self.L = oracle.Layout(params, dp_size, dp_rank, bucket_size, pad_busbw, instances)
         self.nb = self.L.num_buffers
         self.bufs = []
         for k in range(self.nb):

@@ -119,3 +119,27 @@ def test_workload_sizes_are_one_gpu_shares():
             n = b["arena_numel"]
             tot += n * (es[b["grad_dtype"]] + es[b["param_dtype"]] + 8 + (4 if b["param_dtype"] else 0))
         assert tot < 200e9, name
+
+
+@pytest.mark.parametrize("N,I,r", [(16, 2, 11), (64, 8, 37), (8, 8, 5), (12, 3, 7)])
+def test_mapper_matches_oracle_with_instances(N, I, r):
+    d = _dopt()
+    params = PARAM_LISTS["gpt2-small"]()
+    A = d.dopt_build_ranges(params, N, r, 40_000_000, 0, I)
+    B = oracle.Layout(params, N, r, 40_000_000, 0, I)
+    per = N // I
+    assert A.sharding() == {"dp_size": N, "dp_rank": r, "num_instances": I, "instance_size": per,
+                            "instance_index": r // per, "instance_rank": r % per}
+    for k in range(A.num_buffers):
+        a, b = A.buffer(k), B.buffer(k)
+        for key in ("numel", "numel_unpadded", "window_numel", "shard_numel", "n_buckets"):
+            assert a[key] == b[key]
+        for bi in range(a["n_buckets"]):
+            x, y = A.bucket(k, bi), B.bucket(k, bi)
+            assert (x["window_start"], x["shard_size"], x["arena_offset"]) == \
+                   (y["window_start"], y["shard"], y["arena_offset"])
+    for p in range(len(params)):
+        x, y = A.param(p), B.param(p)
+        assert (x["has_shard"], x["arena_offset"], x["param"]) == (y["has_shard"], y["arena_offset"], y["param"])
+    with pytest.raises(d.DoptError):
+        d.dopt_build_ranges(params, 10, 0, 0, 0, 3)

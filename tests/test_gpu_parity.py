@@ -149,3 +149,11 @@ def test_argument_errors_are_reported():
         D.dopt_step(L, [bad], [(1e-3, 0.9, 0.999, 1e-8, 0.0)] * 2, 1.0, A.workspace, stream)
     with pytest.raises(D.DoptError):
         D.dopt_init_state(L, A.bufs, D.scaler_cfg(True, 0.0), A.workspace, stream)
+
+
+def test_instances_gpt2_small():
+    # N=16 split into 2 optimizer instances of 8: rank 11 owns shard 3 of its instance
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.name, case.dp_size, case.dp_rank, case.instances, case.steps = "gpt2-inst", 16, 11, 2, 3
+    rep = H.run_full(case)
+    assert rep[-1]["param0"]["n"] == 15_554_976

@@ -231,3 +231,17 @@ def test_errors():
             oracle.Layout(ps, *args)
     with pytest.raises(oracle.OracleError):
         oracle.Layout([ParamSpec("z", 0, "bf16", "bf16")], 1, 0)
+
+
+@pytest.mark.parametrize("N,I", [(8, 2), (12, 3), (64, 4)])
+def test_instances_own_every_element_once_per_instance(N, I):
+    rng = random.Random(N * 100 + I)
+    params = _random_params(rng, 9, newb_p=0.1)
+    per = N // I
+    for i in range(I):
+        layouts = [oracle.Layout(params, N, r, 700, 0, I) for r in range(i * per, (i + 1) * per)]
+        # within an instance the windows are those of a plain N/I-rank layout
+        _check_partition(params, layouts[0], 700, 0, per)
+        _check_ownership(params, layouts, per)
+    with pytest.raises(oracle.OracleError):
+        oracle.Layout(params, N, 0, 0, 0, N + 1)

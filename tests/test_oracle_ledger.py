@@ -100,3 +100,18 @@ def test_every_element_once_with_padding():
             L = oracle.Layout(params, N, r, 2000)
             tot_state_elems += sum(L.buffer(k)["shard_numel"] for k in range(L.num_buffers))
         assert tot_state_elems == P
+
+
+@pytest.mark.parametrize("N,I", [(8, 2), (64, 8), (16, 16), (6, 3)])
+def test_instances_ledger(N, I):
+    # "02 · ZeRO 显存账本…" §5: with I optimizer instances the 12P of state is cut
+    # to 1/(N/I) per rank, every instance holding one full copy of it.
+    P = 64 * 128 * 48 * 5
+    params = _params(P, 5)
+    per = N // I
+    states = [_state_bytes(oracle.Layout(params, N, r, 0, 0, I)) for r in range(N)]
+    for r in range(N):
+        assert states[r] == 12 * P // per
+    for i in range(I):
+        assert sum(states[i * per:(i + 1) * per]) == 12 * P
+    assert sum(states) == I * 12 * P
