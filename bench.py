@@ -160,6 +160,54 @@ def bench_reduce(args, w, L, A, bufs_c, hp_c, stream):
     }), flush=True)
 
 
+def bench_check(args, w, L, A, stream):
+    """The pre-communication scan of every bucket of the rank's whole local
+    grad buffers (read only)."""
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    bufs, outs, total = [], [], 0
+    for k in range(L.num_buffers):
+        info = L.buffer(k)
+        gd = D.DTYPE_NAMES[info["grad_dtype"]]
+        t = torch.empty(info["numel"], dtype={"f32": torch.float32, "bf16": torch.bfloat16,
+                                              "f16": torch.float16}[gd], device="cuda")
+        t.normal_(0.0, w.grad_sigma, generator=gen)  # seeded synthetic local grads, drawn on the device
+        bufs.append(t)
+        outs.append(torch.zeros(info["n_buckets"] * D.BUCKET_CHECK_BYTES, dtype=torch.uint8, device="cuda"))
+        total += info["numel"] * ES[gd]
+
+    def call():
+        for k in range(L.num_buffers):
+            D.dopt_check_grads(L, k, bufs[k], 1.0, outs[k], A.workspace, stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    gbps = total / (ms * 1e-3) / 1e9
+    numel = sum(L.buffer(k)["numel"] for k in range(L.num_buffers))
+    print(json.dumps({
+        "metric": "whole-bucket NaN/Inf/large-grad scan of a rank's local grad buffers, 1 MI355X",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {numel} buffer elements, "
+                               f"{sum(L.buffer(k)['n_buckets'] for k in range(L.num_buffers))} buckets",
+                   "bytes_per_call": total},
+        "roofline": {"bound": "hbm", "kernel": "k_check (+ k_check_finish)", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_call": total},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,9 +216,10 @@ def main():
     ap.add_argument("--workload", default="gpt2-small")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "reduce"], default="step",
+    ap.add_argument("--mode", choices=["step", "reduce", "check"], default="step",
                     help="step: the optimizer step (default); reduce: the fused local fp32-accumulating reduce of "
-                         "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare)")
+                         "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare); check: the whole-bucket "
+                         "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the step: copy an fp32 buffer of this many MiB (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -224,6 +273,9 @@ def main():
     hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
     if args.mode == "reduce":
         bench_reduce(args, w, L, A, bufs_c, hp_c, stream)
+        return
+    if args.mode == "check":
+        bench_check(args, w, L, A, stream)
         return
 
     # dopt_step = dopt_step_prepare + dopt_step_apply; the two halves are

@@ -337,6 +337,35 @@ int dopt_reduce_prepare(const dopt_layout *layout, const dopt_buffer_tensors *bu
                         int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp,
                         int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream);
 
+/* Result of the pre-communication check of one bucket. */
+typedef struct dopt_bucket_check {
+    double sumsq;     /* sum of squares of the bucket's grads, in double; NaN if any grad is NaN */
+    float max_abs;    /* largest |grad|, NaN ignored; inf if any grad is infinite */
+    int32_t has_nan;  /* some grad is NaN */
+    int32_t has_inf;  /* some grad is +-inf */
+    int32_t large;    /* large_threshold > 0 and max_abs > large_threshold */
+} dopt_bucket_check;
+
+/*
+ * dopt_check_grads -- scan every bucket of flat buffer k of this rank's
+ * local grads (the whole buffer, before the reduce-scatter) for NaN, Inf and
+ * abnormally large values ([DP] §2.4: check_grads of the bucket group; §3.2:
+ * check_for_nan_in_grad, check_for_large_grads).  Readings: the pages do not
+ * define "large"; it is any |grad| above large_threshold (a caller input;
+ * <= 0 turns it off).  The raw buffer values are checked (no unscaling), and
+ * the bucket's padding is part of the scan as it is part of the bucket.
+ *
+ * grad_buffer: device, the full flat buffer k (numel elements of the
+ * buffer's grad dtype, bucket b at its offset).  out: device array of
+ * n_buckets records, written stream-ordered.  Each bucket's partials are
+ * added in a fixed order, so sumsq is deterministic.  The workspace must have
+ * been through dopt_init_state (which loads the bucket tables).
+ * Errors: DOPT_ERR_INVALID (null or misaligned pointers), DOPT_ERR_RANGE (k),
+ * DOPT_ERR_HIP.
+ */
+int dopt_check_grads(const dopt_layout *layout, int32_t k, const void *grad_buffer, double large_threshold,
+                     dopt_bucket_check *out, void *workspace, hipStream_t stream);
+
 /* Byte offset in the workspace of the grad-stats record: two doubles,
  * {sum of squares, zero count}; both are sums over ranks.  A non-finite sum
  * of squares means some rank found an inf/NaN. */

@@ -103,6 +103,8 @@ def _load():
         "or_f16_to_f32_n": ([VP, VP, I64], None),
         "or_init_state": ([VP, P(Arrays)], None),
         "or_reduce_chunks": ([VP, I32, VP, I32, I32, I64, ctypes.c_float, I64, I64, VP], None),
+        "or_check_bucket": ([VP, I32, I32, VP, I64, I64, ctypes.c_double, P(ctypes.c_double), P(ctypes.c_float),
+                             P(I32)], None),
         "or_grad_stats": ([VP, P(Arrays), ctypes.c_float, P(Stats)], None),
         "or_grad_stats_range": ([VP, I32, VP, ctypes.c_float, I64, I64, P(Stats)], None),
         "or_decide": ([P(Stats), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Scalars)], ctypes.c_int),

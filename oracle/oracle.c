@@ -462,6 +462,48 @@ void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Pre-communication check of whole buckets                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [DP] §2.4 (check_grads) and §3.2 (check_for_nan_in_grad,
+ * check_for_large_grads), over the raw values of the buffer elements
+ * [lo, hi) that lie in bucket b of buffer k (the bucket's padding included):
+ * the sum of squares in double in index order, the largest |g| over the
+ * non-NaN values, whether some value is NaN, whether some value is
+ * infinite, and whether the largest |g| exceeds thr (thr > 0; reading: the
+ * pages do not define "large", the threshold is the caller's).
+ * out_flags: has_nan, has_inf, large.
+ */
+void or_check_bucket(const or_layout *L, int32_t k, int32_t b, const void *grad, int64_t lo, int64_t hi, double thr,
+                     double *out_sumsq, float *out_max, int32_t *out_flags) {
+    f16_table_init();
+    const ob_buffer *B = &L->buf[k];
+    const ob_bucket *bk = &B->buckets[b];
+    if (lo < bk->offset) lo = bk->offset;
+    if (hi > bk->offset + bk->numel) hi = bk->offset + bk->numel;
+    double sumsq = 0.0;
+    float mx = 0.0f;
+    int32_t has_nan = 0, has_inf = 0;
+    for (int64_t i = lo; i < hi; ++i) {
+        float g = load_f32(grad, B->gd, i);
+        double gd = (double)g;
+        sumsq += gd * gd;
+        if (isnan(g)) {
+            has_nan = 1;
+            continue;
+        }
+        if (isinf(g)) has_inf = 1;
+        if (fabsf(g) > mx) mx = fabsf(g);
+    }
+    *out_sumsq = sumsq;
+    *out_max = mx;
+    out_flags[0] = has_nan;
+    out_flags[1] = has_inf;
+    out_flags[2] = (thr > 0.0 && (double)mx > thr) ? 1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The step                                                                 */
 /* ------------------------------------------------------------------------ */
 

@@ -92,6 +92,12 @@ void or_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t wire_dtype, int32_t n_chunks,
                       int64_t stride, float scale, int64_t lo, int64_t hi, void *grad_out);
 
+/* ---- pre-communication check of whole buckets ---- */
+/* Over buffer elements [lo, hi) of bucket b of buffer k: sum of squares,
+ * largest |g| (NaN ignored), flags {has_nan, has_inf, max > thr}. */
+void or_check_bucket(const or_layout *L, int32_t k, int32_t b, const void *grad, int64_t lo, int64_t hi, double thr,
+                     double *out_sumsq, float *out_max, int32_t *out_flags);
+
 /* ---- the step ---- */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;

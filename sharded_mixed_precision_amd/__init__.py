@@ -125,6 +125,7 @@ def _load():
         "dopt_step_stats": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
         "dopt_reduce_prepare": ([VP, P(dopt_buffer_tensors), P(VP), I32, I32, ctypes.c_float, P(dopt_hparams), I32, D,
                                  VP, VP], ctypes.c_int),
+        "dopt_check_grads": ([VP, I32, VP, D, VP, VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
         "dopt_stats_record_offset": ([VP], I64),
@@ -143,7 +144,8 @@ EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", 
             "dopt_layout_buffer",
             "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
             "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_prepare", "dopt_step_stats",
-            "dopt_step_finalize", "dopt_step_apply", "dopt_reduce_prepare", "dopt_stats_record_offset",
+            "dopt_step_finalize", "dopt_step_apply", "dopt_reduce_prepare", "dopt_check_grads",
+            "dopt_stats_record_offset",
             "dopt_read_stats",
             "dopt_last_error")
 
@@ -322,6 +324,26 @@ def dopt_reduce_prepare(layout: Layout, bufs, chunks: Sequence, wire_dtype: str,
         nh = len(hp)
     _check(_lib.dopt_reduce_prepare(layout.handle, t, ch, DTYPES[wire_dtype], n_chunks, scale, hp, nh,
                                     max_grad_norm, _addr(workspace), _stream(stream)))
+
+
+class dopt_bucket_check(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("max_abs", ctypes.c_float), ("has_nan", ctypes.c_int32),
+                ("has_inf", ctypes.c_int32), ("large", ctypes.c_int32)]
+
+
+BUCKET_CHECK_BYTES = ctypes.sizeof(dopt_bucket_check)
+
+
+def dopt_check_grads(layout: Layout, k: int, grad_buffer, large_threshold: float, out, workspace, stream=None):
+    """out: device buffer of n_buckets * BUCKET_CHECK_BYTES bytes (e.g. a uint8 CUDA tensor)."""
+    _check(_lib.dopt_check_grads(layout.handle, k, _addr(grad_buffer), large_threshold, _addr(out),
+                                 _addr(workspace), _stream(stream)))
+
+
+def bucket_checks(raw: bytes, n: int) -> List[Dict]:
+    """Decode n dopt_bucket_check records copied to the host."""
+    arr = (dopt_bucket_check * n).from_buffer_copy(raw)
+    return [{name: getattr(r, name) for name, _ in r._fields_} for r in arr]
 
 
 def dopt_step_stats(layout: Layout, bufs, workspace, stream=None):

@@ -40,6 +40,19 @@ struct TileDesc {
     int32_t seg_count;  // number of overlapping segments | kTileFull
 };
 
+// Pre-communication check of whole buckets: a check tile is kCheckTile
+// elements from the bucket start (bucket sizes are multiples of 128
+// elements, so an 8-element vector is either wholly inside a bucket or past
+// its end); one partial per check tile.
+constexpr int64_t kCheckTile = 8 * kTile;
+constexpr int kCheckMaxBlocks = 2048;
+struct CheckBucket {
+    int64_t offset, numel, tile_base;  // tile_base: index of the bucket's first check tile
+};
+struct CheckTile {
+    int64_t start, end;  // the tile's first element and its bucket's end (buffer coordinates)
+};
+
 // A param's shard in arena coordinates, [start, end).
 struct SegDesc {
     int64_t start, end;
@@ -71,6 +84,10 @@ struct Buffer {
     int32_t stats_grid = 0, apply_grid = 0;
     int32_t partial_base = 0;
     int64_t ws_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
+    std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads
+    std::vector<CheckTile> chk_tile;    // per check tile
+    int64_t chk_tiles = 0;
+    int64_t ws_chk = 0, ws_chk_tile = 0, ws_chk_part = 0;
 };
 
 // Workspace map (byte offsets).

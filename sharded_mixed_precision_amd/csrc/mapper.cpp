@@ -189,6 +189,22 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
         ws += align_up(int64_t(B.tiles.size()) * int64_t(sizeof(TileDesc)), 256);
         B.ws_segs = ws;
         ws += align_up(std::max<int64_t>(int64_t(B.segs.size()), 1) * int64_t(sizeof(SegDesc)), 256);
+        // whole-bucket check: the bucket table and one 16-byte partial per check tile
+        B.chk.clear();
+        B.chk_tile.clear();
+        B.chk_tiles = 0;
+        for (const Bucket &bk : B.buckets) {
+            B.chk.push_back(CheckBucket{bk.offset, bk.numel, B.chk_tiles});
+            for (int64_t s = bk.offset; s < bk.offset + bk.numel; s += kCheckTile)
+                B.chk_tile.push_back(CheckTile{s, bk.offset + bk.numel});
+            B.chk_tiles += (bk.numel + kCheckTile - 1) / kCheckTile;
+        }
+        B.ws_chk = ws;
+        ws += align_up(int64_t(B.chk.size()) * int64_t(sizeof(CheckBucket)), 256);
+        B.ws_chk_tile = ws;
+        ws += align_up(B.chk_tiles * int64_t(sizeof(CheckTile)), 256);
+        B.ws_chk_part = ws;
+        ws += align_up(B.chk_tiles * 16, 256);
     }
     L.ws_bytes = ws;
     return DOPT_OK;

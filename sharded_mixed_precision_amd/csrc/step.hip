@@ -18,6 +18,7 @@
 // denormals kept.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 // through pass 1 exactly as in k_stats.  Chunk loads are issued kReduceBatch
 // at a time (the adds stay in chunk order); the chunks are read once, so
 // they are loaded nontemporally.
-constexpr int kReduceBatch = 4;
+constexpr int kReduceBatch = 8;
 
 template <int GD>
 __device__ __forceinline__ float stored_value(float x);
@@ -460,6 +461,128 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
     if (FINALIZE) {
         __syncthreads();
         finalize_block(s_tot[0], s_tot[1], st, sr, out, fa);
+    }
+}
+
+// ---- pre-communication check of whole buckets ---------------------------------
+//
+// [DP] §2.4 (check_grads of a bucket group) and §3.2 (check_for_nan_in_grad,
+// check_for_large_grads), on the raw values of a rank's whole local grad
+// buffer: per bucket the double sum of squares (NaN exactly when some grad
+// is NaN, since g*g is exact in double and cannot overflow it) and the
+// largest |grad| with NaN ignored (infinite exactly when some grad is).
+// k_check writes one partial per check tile, keeping kCheckTile / kTile
+// loads in flight per thread; k_check_finish adds each bucket's partials in
+// tile order (one workgroup per bucket).
+
+struct CheckPartial {
+    double sumsq;
+    float max_abs, pad;
+};
+static_assert(sizeof(CheckPartial) == 16, "check partial size");
+
+constexpr int kCheckLoads = static_cast<int>(kCheckTile / kTile);
+
+template <int GD>
+__global__ void __launch_bounds__(kBlock) k_check(const void *__restrict__ grad, const CheckTile *__restrict__ ct,
+                                                 int64_t n_tiles, CheckPartial *__restrict__ part) {
+    __shared__ double s_acc[kBlock / 64];
+    __shared__ float s_mx[kBlock / 64];
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const int64_t base = ct[t].start;
+        const int64_t end = ct[t].end;
+        float g[kCheckLoads][kVec];
+#pragma unroll
+        for (int u = 0; u < kCheckLoads; ++u) {
+            const int64_t i = base + u * kTile + int64_t(threadIdx.x) * kVec;
+            if (i < end) Elem<GD>::template load8<true>(grad, i, g[u]);
+        }
+        double acc = 0.0;
+        float mx = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kCheckLoads; ++u) {
+            const int64_t i = base + u * kTile + int64_t(threadIdx.x) * kVec;
+            if (i >= end) continue;
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const double xd = static_cast<double>(g[u][j]);
+                acc = fma(xd, xd, acc);
+                mx = fmaxf(mx, fabsf(g[u][j]));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            acc += __shfl_xor(acc, off, 64);
+            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        }
+        __syncthreads();  // the previous tile's totals have been read
+        if ((threadIdx.x & 63) == 0) {
+            s_acc[threadIdx.x >> 6] = acc;
+            s_mx[threadIdx.x >> 6] = mx;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double a = 0.0;
+            float m = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kBlock / 64; ++w) {
+                a += s_acc[w];
+                m = fmaxf(m, s_mx[w]);
+            }
+            part[t].sumsq = a;
+            part[t].max_abs = m;
+            part[t].pad = 0.0f;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) k_check_finish(const CheckPartial *__restrict__ part,
+                                                        const CheckBucket *__restrict__ bk, int32_t n_buckets,
+                                                        int64_t n_tiles, double thr,
+                                                        dopt_bucket_check *__restrict__ out) {
+    const int32_t b = blockIdx.x;
+    const int64_t t0 = bk[b].tile_base;
+    const int64_t t1 = b + 1 < n_buckets ? bk[b + 1].tile_base : n_tiles;
+    double a = 0.0;
+    float m = 0.0f;
+    for (int64_t i0 = t0 + threadIdx.x; i0 < t1; i0 += kFinishBatch * kBlock) {
+        CheckPartial q[kFinishBatch];
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+            const int64_t i = i0 + int64_t(j) * kBlock;
+            q[j] = i < t1 ? part[i] : CheckPartial{0.0, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int j = 0; j < kFinishBatch; ++j) {
+            a += q[j].sumsq;
+            m = fmaxf(m, q[j].max_abs);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+    }
+    __shared__ double s_acc[kBlock / 64];
+    __shared__ float s_mx[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) {
+        s_acc[threadIdx.x >> 6] = a;
+        s_mx[threadIdx.x >> 6] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double sa = 0.0;
+        float sm = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+            sa += s_acc[w];
+            sm = fmaxf(sm, s_mx[w]);
+        }
+        out[b].sumsq = sa;
+        out[b].max_abs = sm;
+        out[b].has_nan = isnan(sa) ? 1 : 0;
+        out[b].has_inf = isinf(sm) ? 1 : 0;
+        out[b].large = (thr > 0.0 && static_cast<double>(sm) > thr) ? 1 : 0;
     }
 }
 
@@ -771,6 +894,14 @@ int dopt_init_state(const dopt_layout *L, const dopt_buffer_tensors *bufs, const
                            "copy segment table");
             if (rc) return rc;
         }
+        rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_chk), B.chk.data(), B.chk.size() * sizeof(CheckBucket),
+                                      hipMemcpyHostToDevice, stream),
+                       "copy bucket table");
+        if (rc) return rc;
+        rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_chk_tile), B.chk_tile.data(),
+                                      B.chk_tile.size() * sizeof(CheckTile), hipMemcpyHostToDevice, stream),
+                       "copy check tile table");
+        if (rc) return rc;
     }
     for (size_t k = 0; k < L->buffers.size(); ++k) {
         const Buffer &B = L->buffers[k];
@@ -857,6 +988,27 @@ int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, c
         return launch_reduce<true>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
     }
     return launch_reduce<false>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
+}
+
+int dopt_check_grads(const dopt_layout *L, int32_t k, const void *grad, double thr, dopt_bucket_check *out, void *ws,
+                     hipStream_t stream) {
+    if (!L || !grad || !out || !ws) return fail(DOPT_ERR_INVALID, "null layout, grad buffer, output or workspace");
+    if (k < 0 || k >= static_cast<int32_t>(L->buffers.size())) return fail(DOPT_ERR_RANGE, "buffer index");
+    if (!aligned(grad) || !aligned(ws) || reinterpret_cast<uintptr_t>(out) % 8 != 0)
+        return fail(DOPT_ERR_INVALID, "grad buffer or workspace not 256-byte aligned, or output not 8-byte aligned");
+    const Buffer &B = L->buffers[k];
+    const CheckBucket *bk = reinterpret_cast<const CheckBucket *>(ws_ptr(ws, B.ws_chk));
+    const CheckTile *ct = reinterpret_cast<const CheckTile *>(ws_ptr(ws, B.ws_chk_tile));
+    CheckPartial *part = reinterpret_cast<CheckPartial *>(ws_ptr(ws, B.ws_chk_part));
+    const int32_t nb = static_cast<int32_t>(B.chk.size());
+    const dim3 grid(static_cast<uint32_t>(std::min<int64_t>(B.chk_tiles, kCheckMaxBlocks)));
+    if (B.gd == DOPT_BF16) k_check<DOPT_BF16><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
+    else if (B.gd == DOPT_F16) k_check<DOPT_F16><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
+    else k_check<DOPT_F32><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
+    int rc = check_launch("launch k_check");
+    if (rc) return rc;
+    k_check_finish<<<nb, kBlock, 0, stream>>>(part, bk, nb, B.chk_tiles, thr, out);
+    return check_launch("launch k_check_finish");
 }
 
 int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream) {

@@ -28,6 +28,7 @@ STREAM_GRAD = 2
 STREAM_ZERO_MASK = 3
 STREAM_INF_POS = 4
 STREAM_CHUNK = 5
+STREAM_LOCAL_GRAD = 6
 _BUFFER_STRIDE = 64  # stream offset between flat buffers
 
 
@@ -83,6 +84,11 @@ def weight_stream(buffer_index: int) -> int:
 
 def grad_stream(buffer_index: int) -> int:
     return buffer_stream(STREAM_GRAD, buffer_index)
+
+
+def local_grad_stream(buffer_index: int) -> int:
+    """Stream of a rank's whole local (pre-communication) grad buffer."""
+    return buffer_stream(STREAM_LOCAL_GRAD, buffer_index)
 
 
 def chunk_stream(buffer_index: int) -> int:

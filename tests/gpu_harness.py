@@ -376,6 +376,85 @@ def oracle_reduce_parallel(O: oracle.Layout, k: int, chunks: torch.Tensor, wire:
         list(ex.map(run, range(0, n, chunk)))
 
 
+def oracle_check_parallel(O: oracle.Layout, k: int, grad: torch.Tensor, thr: float, workers: int = 16,
+                          chunk: int = 1 << 24) -> List[dict]:
+    """The oracle's whole-bucket check of buffer k; each bucket split into
+    disjoint element ranges run on host threads and combined in range order."""
+    lib = oracle.lib()
+    nb = O.buffer(k)["n_buckets"]
+    jobs = []
+    for b in range(nb):
+        bk = O.bucket(k, b)
+        for lo in range(bk["offset"], bk["offset"] + bk["numel"], chunk):
+            jobs.append((b, lo, min(lo + chunk, bk["offset"] + bk["numel"])))
+
+    def run(job):
+        b, lo, hi = job
+        s, m, f = ctypes.c_double(), ctypes.c_float(), (ctypes.c_int32 * 3)()
+        lib.or_check_bucket(O.handle, k, b, grad.data_ptr(), lo, hi, thr, ctypes.byref(s), ctypes.byref(m), f)
+        return b, s.value, m.value, tuple(f)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(run, jobs))
+    out = [{"sumsq": 0.0, "max_abs": 0.0, "has_nan": 0, "has_inf": 0, "large": 0} for _ in range(nb)]
+    for b, s, m, f in parts:
+        o = out[b]
+        o["sumsq"] += s
+        o["max_abs"] = max(o["max_abs"], m)
+        o["has_nan"] |= f[0]
+        o["has_inf"] |= f[1]
+        o["large"] |= f[2]
+    return out
+
+
+def check_bucket_results(dev: List[dict], ref: List[dict], where: str):
+    assert len(dev) == len(ref), where
+    for b, (x, y) in enumerate(zip(dev, ref)):
+        for key in ("has_nan", "has_inf", "large"):
+            assert x[key] == y[key], (where, b, key, x, y)
+        assert np.float32(x["max_abs"]) == np.float32(y["max_abs"]), (where, b, x, y)
+        if math.isfinite(y["sumsq"]):
+            assert math.isclose(x["sumsq"], y["sumsq"], rel_tol=1e-10, abs_tol=0.0), (where, b, x, y)
+        else:
+            assert math.isnan(x["sumsq"]) == math.isnan(y["sumsq"]) and not math.isfinite(x["sumsq"]), (where, b)
+
+
+def run_check(case: Case, thr: float, injections=()) -> List[List[dict]]:
+    """Whole local grad buffers through dopt_check_grads and the oracle.
+    injections: (buffer, element index, value) written into the buffer first."""
+    D = _dopt()
+    from sharded_mixed_precision_amd.arena import DeviceArenas
+    t0 = time.time()
+    L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, case.instances)
+    O = oracle.Layout(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, case.instances)
+    A = DeviceArenas(L)
+    stream = torch.cuda.current_stream()
+    D.dopt_init_state(L, A.bufs, D.scaler_cfg(), A.workspace, stream)
+    results = []
+    for k in range(L.num_buffers):
+        info = L.buffer(k)
+        gd = {0: "f32", 1: "bf16", 2: "f16"}[info["grad_dtype"]]
+        n = info["numel"]
+        host = synth.fill_normal(gd, n, case.seed, synth.local_grad_stream(k), 1, case.grad_sigma,
+                                 zero_frac=case.zero_frac, out=torch.empty(n, dtype=synth.torch_dtype(gd),
+                                                                           pin_memory=True))
+        for kk, i, val in injections:
+            if kk == k:
+                host[i] = val
+        dev = torch.empty(n, dtype=host.dtype, device="cuda")
+        dev.copy_(host)
+        nb = info["n_buckets"]
+        out = torch.zeros(nb * D.BUCKET_CHECK_BYTES, dtype=torch.uint8, device="cuda")
+        D.dopt_check_grads(L, k, dev, thr, out, A.workspace, stream)
+        got = D.bucket_checks(out.cpu().numpy().tobytes(), nb)
+        ref = oracle_check_parallel(O, k, host, thr)
+        check_bucket_results(got, ref, f"{case.name} buffer {k}")
+        results.append(got)
+        del dev
+    log(f"[check] {case.name}: {sum(len(r) for r in results)} buckets ok in {time.time() - t0:.1f}s")
+    return results
+
+
 def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
     """Full-size run on the device; the oracle computes the exact per-step
     stats over all shard elements and the trajectories of sampled elements."""

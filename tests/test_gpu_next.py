@@ -51,6 +51,36 @@ def test_reduce_llama3_8b_sampled():
     H.run_sampled(case)
 
 
+def test_check_gpt2_small_buffer_with_injections():
+    # the whole local bf16 grad buffer of the GPT-2-small rank (124,439,808
+    # elements, 3 buckets): a NaN in bucket 1, an infinity in bucket 2, a large
+    # value in bucket 0, NaN and infinity together in a second case
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.grad_sigma = 1e-3
+    from sharded_mixed_precision_amd import dopt_build_ranges
+    L = dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size)
+    off = [L.bucket(0, b)["offset"] for b in range(3)]
+    res = H.run_check(case, 0.5, [(0, off[0] + 12345, 3.0), (0, off[1] + 777, float("nan")),
+                                  (0, off[2] + 5, float("-inf"))])[0]
+    assert [(r["has_nan"], r["has_inf"], r["large"]) for r in res] == [(0, 0, 1), (1, 0, 0), (0, 1, 1)]
+    res = H.run_check(case, 0.0, [(0, off[1] + 1, float("nan")), (0, off[1] + 2, float("inf"))])[0]
+    assert [(r["has_nan"], r["has_inf"], r["large"]) for r in res] == [(0, 0, 0), (1, 1, 0), (0, 0, 0)]
+
+
+def test_check_mixed_buffers_odd_sizes():
+    params = [ParamSpec("a", 50000, "bf16", "f32"), ParamSpec("n", 300, "f32", "f32"),
+              ParamSpec("h", 70001, "f16", "f16"), ParamSpec("b", 777, "bf16", "f32")]
+    H.run_check(H.Case("check-mixed", params, 96, 5, 20000, grad_sigma=1.0), 3.0)
+
+
+@pytest.mark.timeout(600)
+def test_check_dense_7b_buffer():
+    # the whole fp16 buffer of the dense 7B model (6,738,415,616 elements, 130 buckets)
+    case = H.case_from_workload(synth.WORKLOADS["dense-7b"])
+    res = H.run_check(case, 4.0e-3, [(0, 123_456_789, float("inf"))])[0]
+    assert len(res) == 130 and sum(r["has_inf"] for r in res) == 1
+
+
 def test_reduce_argument_errors():
     import sharded_mixed_precision_amd as D
     from sharded_mixed_precision_amd.arena import DeviceArenas
