@@ -208,6 +208,50 @@ def bench_check(args, w, L, A, stream):
     }), flush=True)
 
 
+def bench_checkpoint(args, w, L, A, bufs_c, stream):
+    """Model-space export of the rank's (master, m, v) shards and the import
+    back (which also rewrites the 16-bit params from the master)."""
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    n = L.state_numel
+    ex = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    exp_bytes = imp_bytes = 0
+    for info in A.info:
+        exp_bytes += 24 * info["shard_numel"]  # read master, m, v; write three fp32 exports
+        imp_bytes += (24 + (ES[info["pd"]] if info["pd"] != "f32" else 0)) * info["shard_numel"]
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    ms_e = timed(lambda: D.dopt_state_export(L, bufs_c, *ex, A.workspace, stream))
+    ms_i = timed(lambda: D.dopt_state_import(L, bufs_c, *ex, A.workspace, stream))
+    ge = exp_bytes / (ms_e * 1e-3) / 1e9
+    gi = imp_bytes / (ms_i * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "model-space optimizer-state export of a rank's (master, m, v) shards, 1 MI355X",
+        "value": round(ge, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_call": round(ms_e, 5), "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank {w.dp_rank} of N={w.dp_size}, {n} shard elements",
+                   "bytes_per_call": exp_bytes},
+        "roofline": {"bound": "hbm", "kernel": "k_state_copy (export)", "achieved": round(ge, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ge / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_call": exp_bytes},
+        "import": {"ms_per_call": round(ms_i, 5), "GBps": round(gi, 1), "frac": round(gi / HBM_PEAK_GBPS, 4),
+                   "algorithmic_bytes_per_call": imp_bytes},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,10 +260,11 @@ def main():
     ap.add_argument("--workload", default="gpt2-small")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "reduce", "check"], default="step",
+    ap.add_argument("--mode", choices=["step", "reduce", "check", "checkpoint"], default="step",
                     help="step: the optimizer step (default); reduce: the fused local fp32-accumulating reduce of "
                          "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare); check: the whole-bucket "
-                         "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads)")
+                         "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads); checkpoint: the "
+                         "model-space export and import of the rank's optimizer state (dopt_state_export / _import)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the step: copy an fp32 buffer of this many MiB (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -276,6 +321,9 @@ def main():
         return
     if args.mode == "check":
         bench_check(args, w, L, A, stream)
+        return
+    if args.mode == "checkpoint":
+        bench_checkpoint(args, w, L, A, bufs_c, stream)
         return
 
     # dopt_step = dopt_step_prepare + dopt_step_apply; the two halves are

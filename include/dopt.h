@@ -176,6 +176,7 @@ typedef struct dopt_param_info {
     dopt_range gbuf_local;      /* shard, window coordinates */
     dopt_range param;           /* shard, coordinates inside the param */
     int64_t arena_offset;       /* shard start in the arena; -1 without a shard */
+    int64_t export_offset;      /* shard start in the model-space export (dopt_state_export); -1 without */
 } dopt_param_info;
 
 int32_t dopt_layout_num_buffers(const dopt_layout *layout);
@@ -365,6 +366,44 @@ typedef struct dopt_bucket_check {
  */
 int dopt_check_grads(const dopt_layout *layout, int32_t k, const void *grad_buffer, double large_threshold,
                      dopt_bucket_check *out, void *workspace, hipStream_t stream);
+
+/*
+ * Sharded optimizer-state checkpoint in model-parameter space.  [DO] "三层继承
+ * 体系" (third layer) lists fully reshardable optimizer formats: formats that
+ * do not depend on the internal optimizer buffer structure.  The export
+ * space of a rank is its param shards in model order, each shard contiguous
+ * and in param coordinates (dopt_param_info.param), at
+ * dopt_param_info.export_offset; it holds dopt_layout_state_numel()
+ * elements.  Any other bucketing, data-parallel size or rank can read the
+ * state it owns from the union of all ranks' exports.  Reading: the pages
+ * name the formats only; this is the plainest model-space form.
+ *
+ * dopt_state_export: master (for fp32 params: the param itself), m and v of
+ *   every shard element -> three device fp32 arrays of state_numel elements.
+ * dopt_state_import: the inverse; also rewrites the param window from the
+ *   imported master (round to nearest even for 16-bit params), as the step's
+ *   copy-back would.
+ * Both are stream-ordered device copies; the workspace must have been
+ * through dopt_init_state.  Errors: DOPT_ERR_INVALID, DOPT_ERR_HIP.
+ */
+int dopt_state_export(const dopt_layout *layout, const dopt_buffer_tensors *bufs, float *master, float *exp_avg,
+                      float *exp_avg_sq, void *workspace, hipStream_t stream);
+int dopt_state_import(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const float *master,
+                      const float *exp_avg, const float *exp_avg_sq, void *workspace, hipStream_t stream);
+
+/* The scalar optimizer state kept in the workspace. */
+typedef struct dopt_state_scalars {
+    int64_t step_count;          /* successful steps (Adam's t) */
+    double loss_scale;
+    int64_t growth_tracker;
+    int64_t hysteresis_tracker;
+} dopt_state_scalars;
+
+/* Read / overwrite the scalar state (host struct); both synchronize `stream`. */
+int dopt_state_scalars_get(const dopt_layout *layout, const void *workspace, hipStream_t stream,
+                           dopt_state_scalars *out);
+int dopt_state_scalars_set(const dopt_layout *layout, void *workspace, hipStream_t stream,
+                           const dopt_state_scalars *in);
 
 /* Byte offset in the workspace of the grad-stats record: two doubles,
  * {sum of squares, zero count}; both are sums over ranks.  A non-finite sum

@@ -112,6 +112,8 @@ def _load():
         "or_apply_elems": ([I32, I32, I64, VP, VP, VP, VP, VP, VP, P(Scalars)], None),
         "or_step": ([VP, P(Arrays), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Stats)], ctypes.c_int),
         "or_inv_scale": ([P(Scaler)], ctypes.c_float),
+        "or_state_export": ([VP, P(Arrays), VP, VP, VP], I64),
+        "or_state_import": ([VP, P(Arrays), VP, VP, VP], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)

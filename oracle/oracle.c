@@ -729,3 +729,60 @@ int or_step(const or_layout *L, or_arrays *bufs, or_scaler *sc, int64_t *t, cons
     or_apply(L, bufs, &s);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Model-space optimizer-state checkpoint                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [DO] "三层继承体系", third layer: the DistributedOptimizer class lists the
+ * checkpoint formats that are fully reshardable, i.e. do not depend on how
+ * the optimizer buffers are laid out; one is in model space.  Reading: the
+ * pages give the formats' names only.  Plainest model-space form: walk the
+ * params in model order; each param that has a shard on this rank contributes
+ * its shard, in param coordinates, as one contiguous run of the export; per
+ * element the export holds the fp32 master (the param itself for fp32
+ * params), m and v.  Any layout (other N, rank or bucketing) recovers its own
+ * shards from the union of all ranks' exports by param coordinates.
+ * Returns the number of exported elements.
+ */
+int64_t or_state_export(const or_layout *L, const or_arrays *bufs, float *master, float *m, float *v) {
+    int64_t x = 0;
+    for (int64_t i = 0; i < L->n_params; ++i) {
+        const ob_param *p = &L->p[i];
+        if (!p->has_shard) continue;
+        const or_arrays *b = &bufs[p->buffer];
+        const float *pm = p->pd == OR_F32 ? (const float *)b->param : b->master;
+        for (int64_t j = 0; j < p->prange[1] - p->prange[0]; ++j, ++x) {
+            master[x] = pm[p->arena + j];
+            m[x] = b->m[p->arena + j];
+            v[x] = b->v[p->arena + j];
+        }
+    }
+    return x;
+}
+
+/*
+ * Inverse of or_state_export.  Loading the master also refreshes the 16-bit
+ * model param from it (round to nearest even), the same copy-back the
+ * update ends with ([DO] "三层继承体系", second layer).
+ */
+void or_state_import(const or_layout *L, or_arrays *bufs, const float *master, const float *m, const float *v) {
+    int64_t x = 0;
+    for (int64_t i = 0; i < L->n_params; ++i) {
+        const ob_param *p = &L->p[i];
+        if (!p->has_shard) continue;
+        or_arrays *b = &bufs[p->buffer];
+        for (int64_t j = 0; j < p->prange[1] - p->prange[0]; ++j, ++x) {
+            const int64_t e = p->arena + j;
+            if (p->pd == OR_F32) {
+                ((float *)b->param)[e] = master[x];
+            } else {
+                b->master[e] = master[x];
+                store_param(b->param, p->pd, e, master[x]);
+            }
+            b->m[e] = m[x];
+            b->v[e] = v[x];
+        }
+    }
+}

@@ -159,6 +159,14 @@ int or_step(const or_layout *L, or_arrays *bufs, or_scaler *sc, int64_t *t, cons
             int32_t nh, double max_norm, or_stats *out);
 float or_inv_scale(const or_scaler *sc);
 
+/* ---- model-space optimizer-state checkpoint ---- */
+/* The rank's shards of master (fp32 params: the param), m and v, params in
+ * model order, each shard contiguous in param coordinates.  Returns the
+ * element count. */
+int64_t or_state_export(const or_layout *L, const or_arrays *bufs, float *master, float *m, float *v);
+/* Inverse; also writes the 16-bit params from the imported master. */
+void or_state_import(const or_layout *L, or_arrays *bufs, const float *master, const float *m, const float *v);
+
 #ifdef __cplusplus
 }
 #endif

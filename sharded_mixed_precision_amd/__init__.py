@@ -72,7 +72,7 @@ class dopt_param_info(ctypes.Structure):
     _fields_ = [("buffer", ctypes.c_int32), ("bucket", ctypes.c_int32), ("has_shard", ctypes.c_int32),
                 ("hgroup", ctypes.c_int32), ("start", ctypes.c_int64), ("end", ctypes.c_int64),
                 ("gbuf_world", dopt_range), ("gbuf_world_in_bucket", dopt_range), ("gbuf_local", dopt_range),
-                ("param", dopt_range), ("arena_offset", ctypes.c_int64)]
+                ("param", dopt_range), ("arena_offset", ctypes.c_int64), ("export_offset", ctypes.c_int64)]
 
 
 class dopt_buffer_tensors(ctypes.Structure):
@@ -89,6 +89,11 @@ class dopt_scaler_cfg(ctypes.Structure):
 class dopt_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class dopt_state_scalars(ctypes.Structure):
+    _fields_ = [("step_count", ctypes.c_int64), ("loss_scale", ctypes.c_double),
+                ("growth_tracker", ctypes.c_int64), ("hysteresis_tracker", ctypes.c_int64)]
 
 
 class dopt_stats(ctypes.Structure):
@@ -128,6 +133,10 @@ def _load():
         "dopt_check_grads": ([VP, I32, VP, D, VP, VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
+        "dopt_state_export": ([VP, P(dopt_buffer_tensors), VP, VP, VP, VP, VP], ctypes.c_int),
+        "dopt_state_import": ([VP, P(dopt_buffer_tensors), VP, VP, VP, VP, VP], ctypes.c_int),
+        "dopt_state_scalars_get": ([VP, VP, VP, P(dopt_state_scalars)], ctypes.c_int),
+        "dopt_state_scalars_set": ([VP, VP, VP, P(dopt_state_scalars)], ctypes.c_int),
         "dopt_stats_record_offset": ([VP], I64),
         "dopt_read_stats": ([VP, VP, VP, P(dopt_stats)], ctypes.c_int),
         "dopt_last_error": ([], ctypes.c_char_p),
@@ -145,6 +154,7 @@ EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", 
             "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
             "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_prepare", "dopt_step_stats",
             "dopt_step_finalize", "dopt_step_apply", "dopt_reduce_prepare", "dopt_check_grads",
+            "dopt_state_export", "dopt_state_import", "dopt_state_scalars_get", "dopt_state_scalars_set",
             "dopt_stats_record_offset",
             "dopt_read_stats",
             "dopt_last_error")
@@ -365,6 +375,32 @@ def dopt_read_stats(layout: Layout, workspace, stream=None) -> Dict:
     st = dopt_stats()
     _check(_lib.dopt_read_stats(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
     return st.as_dict()
+
+
+def dopt_state_export(layout: Layout, bufs, master, exp_avg, exp_avg_sq, workspace, stream=None):
+    """Write the rank's (master, m, v) shards in model order into three fp32
+    device arrays of layout.state_numel() elements."""
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    _check(_lib.dopt_state_export(layout.handle, t, _addr(master), _addr(exp_avg), _addr(exp_avg_sq),
+                                  _addr(workspace), _stream(stream)))
+
+
+def dopt_state_import(layout: Layout, bufs, master, exp_avg, exp_avg_sq, workspace, stream=None):
+    """Inverse of dopt_state_export; also rewrites the param window from the master."""
+    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    _check(_lib.dopt_state_import(layout.handle, t, _addr(master), _addr(exp_avg), _addr(exp_avg_sq),
+                                  _addr(workspace), _stream(stream)))
+
+
+def dopt_state_scalars_get(layout: Layout, workspace, stream=None) -> Dict:
+    st = dopt_state_scalars()
+    _check(_lib.dopt_state_scalars_get(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
+    return {name: getattr(st, name) for name, _ in st._fields_}
+
+
+def dopt_state_scalars_set(layout: Layout, workspace, scalars: Dict, stream=None):
+    st = dopt_state_scalars(**scalars)
+    _check(_lib.dopt_state_scalars_set(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
 
 
 def dopt_last_error() -> str:

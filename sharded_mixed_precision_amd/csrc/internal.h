@@ -53,10 +53,12 @@ struct CheckTile {
     int64_t start, end;  // the tile's first element and its bucket's end (buffer coordinates)
 };
 
-// A param's shard in arena coordinates, [start, end).
+// A param's shard in arena coordinates, [start, end), and where it sits in
+// the model-space state export.
 struct SegDesc {
     int64_t start, end;
-    int32_t hgroup, pad;
+    int64_t xoff;
+    int32_t hgroup, param;
 };
 
 struct Bucket {
@@ -72,6 +74,7 @@ struct Param {
     int32_t has_shard = 0;
     dopt_range world{0, 0}, world_in_bucket{0, 0}, local{0, 0}, prange{0, 0};
     int64_t arena = -1;
+    int64_t xoff = -1;  // offset of the shard in the model-space export
 };
 
 struct Buffer {

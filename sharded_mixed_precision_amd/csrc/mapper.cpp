@@ -113,7 +113,7 @@ static void map_windows(dopt_layout &L, Buffer &B) {
         p.prange = {sub, sub + (hi - lo)};
         p.arena = bk.arena_offset + lo;
         B.shard_numel += hi - lo;
-        B.segs.push_back(SegDesc{p.arena, p.arena + (hi - lo), p.hgroup, 0});
+        B.segs.push_back(SegDesc{p.arena, p.arena + (hi - lo), -1, p.hgroup, static_cast<int32_t>(pi)});
     }
     std::sort(B.segs.begin(), B.segs.end(), [](const SegDesc &a, const SegDesc &b) { return a.start < b.start; });
 }
@@ -183,6 +183,15 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
         L.state_numel += B.shard_numel;
     }
     L.total_partials = partials;
+    // model-space export: the shards in model order, back to back
+    int64_t xoff = 0;
+    for (Param &p : L.params) {
+        if (!p.has_shard) continue;
+        p.xoff = xoff;
+        xoff += p.local.end - p.local.start;
+    }
+    for (Buffer &B : L.buffers)
+        for (SegDesc &s : B.segs) s.xoff = L.params[s.param].xoff;
     ws += align_up(int64_t(partials) * 16, 256);
     for (Buffer &B : L.buffers) {
         B.ws_tiles = ws;
@@ -318,6 +327,7 @@ int dopt_layout_param(const dopt_layout *L, int64_t p, dopt_param_info *out) {
         out->param = q.prange;
     }
     out->arena_offset = q.has_shard ? q.arena : -1;
+    out->export_offset = q.has_shard ? q.xoff : -1;
     return DOPT_OK;
 }
 

@@ -666,6 +666,46 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
     }
 }
 
+// ---- model-space state export / import -------------------------------------------
+//
+// Every shard element e of the arena corresponds to export slot
+// xoff(seg) + (e - seg.start).  Lane l of a workgroup takes elements
+// tile*kTile + j*kBlock + l (j = 0..7), so a wave touches 64 consecutive
+// arena slots and, within one segment, 64 consecutive export slots.
+template <int PD, bool IMPORT>
+__global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param, float *__restrict__ master,
+                                                      float *__restrict__ m, float *__restrict__ v,
+                                                      const TileDesc *__restrict__ tiles,
+                                                      const SegDesc *__restrict__ segs, int64_t n_tiles,
+                                                      float *__restrict__ xm, float *__restrict__ xa,
+                                                      float *__restrict__ xv) {
+    float *pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const TileDesc td = tiles[t];
+        const int32_t cnt = td.seg_count & kTileCountMask;
+        if (cnt == 0) continue;
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t e = t * kTile + int64_t(j) * kBlock + threadIdx.x;
+            int32_t s = td.seg_first;
+            if (!(td.seg_count & kTileFull)) {
+                while (s < td.seg_first + cnt && !(segs[s].start <= e && e < segs[s].end)) ++s;
+                if (s == td.seg_first + cnt) continue;  // alignment gap, padding or arena tail
+            }
+            const int64_t x = segs[s].xoff + (e - segs[s].start);
+            if (IMPORT) {
+                pm[e] = xm[x];
+                m[e] = xa[x];
+                v[e] = xv[x];
+                if (PD != DOPT_F32) Elem<PD>::store1(param, e, xm[x]);
+            } else {
+                xm[x] = pm[e];
+                xa[x] = m[e];
+                xv[x] = v[e];
+            }
+        }
+    }
+}
+
 // ---- state init ---------------------------------------------------------------
 // [DO] "分片切片逻辑": the fp32 master is the 16-bit shard converted to float;
 // Adam moments start at zero.
@@ -866,6 +906,33 @@ static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, 
     return launch_finish<FINALIZE>(L, ws, stream, fa);
 }
 
+template <bool IMPORT>
+static int state_copy(const dopt_layout *L, const dopt_buffer_tensors *bufs, float *xm, float *xa, float *xv,
+                      void *ws, hipStream_t stream) {
+    int rc = check_bufs(L, bufs, ws, false);
+    if (rc != DOPT_OK) return rc;
+    if (!xm || !xa || !xv) return fail(DOPT_ERR_INVALID, "null export array");
+    for (size_t k = 0; k < L->buffers.size(); ++k) {
+        const Buffer &B = L->buffers[k];
+        const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
+        const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
+        const int64_t n_tiles = B.arena_numel / kTile;
+        const dim3 grid(B.apply_grid);
+        const dopt_buffer_tensors &b = bufs[k];
+        if (B.pd == DOPT_BF16)
+            k_state_copy<DOPT_BF16, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, b.master, b.exp_avg, b.exp_avg_sq,
+                                                                         tiles, segs, n_tiles, xm, xa, xv);
+        else if (B.pd == DOPT_F16)
+            k_state_copy<DOPT_F16, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, b.master, b.exp_avg, b.exp_avg_sq,
+                                                                        tiles, segs, n_tiles, xm, xa, xv);
+        else
+            k_state_copy<DOPT_F32, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, nullptr, b.exp_avg, b.exp_avg_sq,
+                                                                        tiles, segs, n_tiles, xm, xa, xv);
+        if ((rc = check_launch("launch k_state_copy"))) return rc;
+    }
+    return DOPT_OK;
+}
+
 }  // namespace dopt
 
 using namespace dopt;
@@ -1009,6 +1076,51 @@ int dopt_check_grads(const dopt_layout *L, int32_t k, const void *grad, double t
     if (rc) return rc;
     k_check_finish<<<nb, kBlock, 0, stream>>>(part, bk, nb, B.chk_tiles, thr, out);
     return check_launch("launch k_check_finish");
+}
+
+int dopt_state_export(const dopt_layout *L, const dopt_buffer_tensors *bufs, float *master, float *exp_avg,
+                      float *exp_avg_sq, void *ws, hipStream_t stream) {
+    return state_copy<false>(L, bufs, master, exp_avg, exp_avg_sq, ws, stream);
+}
+
+int dopt_state_import(const dopt_layout *L, const dopt_buffer_tensors *bufs, const float *master,
+                      const float *exp_avg, const float *exp_avg_sq, void *ws, hipStream_t stream) {
+    return state_copy<true>(L, bufs, const_cast<float *>(master), const_cast<float *>(exp_avg),
+                            const_cast<float *>(exp_avg_sq), ws, stream);
+}
+
+int dopt_state_scalars_get(const dopt_layout *L, const void *ws, hipStream_t stream, dopt_state_scalars *out) {
+    if (!L || !ws || !out) return fail(DOPT_ERR_INVALID, "null layout, workspace or output");
+    DevState st;
+    int rc = hip_check(hipMemcpyAsync(&st, static_cast<const char *>(ws) + kWsState, sizeof st,
+                                      hipMemcpyDeviceToHost, stream),
+                       "copy scalar state");
+    if (rc) return rc;
+    if ((rc = hip_check(hipStreamSynchronize(stream), "synchronize for scalar state"))) return rc;
+    out->step_count = st.t;
+    out->loss_scale = st.scale;
+    out->growth_tracker = st.growth_tracker;
+    out->hysteresis_tracker = st.hysteresis_tracker;
+    return DOPT_OK;
+}
+
+int dopt_state_scalars_set(const dopt_layout *L, void *ws, hipStream_t stream, const dopt_state_scalars *in) {
+    if (!L || !ws || !in) return fail(DOPT_ERR_INVALID, "null layout, workspace or input");
+    if (!(in->loss_scale > 0.0) || in->step_count < 0) return fail(DOPT_ERR_INVALID, "bad scalar state");
+    DevState st;
+    int rc = hip_check(hipMemcpyAsync(&st, ws_ptr(ws, kWsState), sizeof st, hipMemcpyDeviceToHost, stream),
+                       "copy scalar state");
+    if (rc) return rc;
+    if ((rc = hip_check(hipStreamSynchronize(stream), "synchronize for scalar state"))) return rc;
+    st.t = in->step_count;
+    st.scale = in->loss_scale;
+    st.inv_scale = static_cast<float>(1.0 / in->loss_scale);
+    st.growth_tracker = in->growth_tracker;
+    st.hysteresis_tracker = in->hysteresis_tracker;
+    if ((rc = hip_check(hipMemcpyAsync(ws_ptr(ws, kWsState), &st, sizeof st, hipMemcpyHostToDevice, stream),
+                        "write scalar state")))
+        return rc;
+    return hip_check(hipStreamSynchronize(stream), "synchronize after scalar state");
 }
 
 int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void *ws, hipStream_t stream) {

@@ -25,7 +25,8 @@ import torch
 
 import oracle
 import synth
-from tests.oracle_harness import OracleRun, to_bits
+from tests.oracle_harness import (NP_STORE, OracleRun, export_to_model, model_to_export, place_in_arenas,
+                                  shard_pieces, to_bits, to_torch)
 
 MASTER_RTOL, MASTER_ATOL = 1e-6, 1e-9
 NORM_RTOL = 1e-5
@@ -548,3 +549,107 @@ def run_sampled(case: Case, n_samples: int = 1 << 20) -> List[dict]:
             f"{time.time() - to:.1f}s; {rep}")
     log(f"[parity] {case.name}: sampled compare ok in {time.time() - t0:.1f}s")
     return report
+
+
+# --------------------------------------------------- multi-rank and reshard ---
+
+class DeviceRanks:
+    """All N ranks of a data-parallel job on the one device, each with its own
+    layout, arenas and workspace, joined through the library's cross-rank seam:
+    dopt_step_stats on every rank, the grad-stats records summed over ranks in
+    rank order (the all-reduce a real job makes), dopt_step_finalize and
+    dopt_step_apply on every rank."""
+
+    def __init__(self, params, dp_size, bucket_size=0, scaler=(False, 1.0)):
+        D = _dopt()
+        from sharded_mixed_precision_amd.arena import DeviceArenas
+        self.D, self.params = D, list(params)
+        self.layouts = [D.dopt_build_ranges(self.params, dp_size, r, bucket_size) for r in range(dp_size)]
+        self.arenas = [DeviceArenas(L) for L in self.layouts]
+        self.stream = torch.cuda.current_stream()
+        self.scaler = scaler
+        self.rec_off = self.layouts[0].stats_record_offset
+
+    def _host_arenas(self, A, key, dtkey):
+        return [np.zeros(info["n"], NP_STORE[info[dtkey]]) for info in A.info]
+
+    def init(self, weights):
+        for L, A in zip(self.layouts, self.arenas):
+            host = self._host_arenas(A, "param", "pd")
+            place_in_arenas(L, len(self.params), [to_bits(w) for w in weights], host)
+            for k, h in enumerate(host):
+                A.bufs[k]["param"].copy_(to_torch(h, A.info[k]["pd"]))
+            self.D.dopt_init_state(L, A.bufs, self.D.scaler_cfg(*self.scaler), A.workspace, self.stream)
+
+    def _record(self, A):
+        return A.workspace[self.rec_off:self.rec_off + 16].view(torch.float64)
+
+    def step(self, grads, hparams, max_norm) -> dict:
+        D = self.D
+        gbits = [to_bits(g) for g in grads]
+        for L, A in zip(self.layouts, self.arenas):
+            host = self._host_arenas(A, "grad", "gd")
+            place_in_arenas(L, len(self.params), gbits, host)
+            for k, h in enumerate(host):
+                A.bufs[k]["grad"].copy_(to_torch(h, A.info[k]["gd"]))
+            D.dopt_step_stats(L, A.bufs, A.workspace, self.stream)
+        sumsq, zeros = 0.0, 0.0
+        for A in self.arenas:  # rank order
+            r = self._record(A).cpu().tolist()
+            sumsq += r[0]
+            zeros += r[1]
+        total = torch.tensor([sumsq, zeros], dtype=torch.float64)
+        for L, A in zip(self.layouts, self.arenas):
+            self._record(A).copy_(total)
+            D.dopt_step_finalize(L, hparams, max_norm, A.workspace, self.stream)
+            D.dopt_step_apply(L, A.bufs, A.workspace, self.stream)
+        stats = [D.dopt_read_stats(L, A.workspace, self.stream) for L, A in zip(self.layouts, self.arenas)]
+        for s in stats[1:]:
+            assert s == stats[0], "ranks disagree on the step's scalars"
+        return stats[0]
+
+    def model_state(self):
+        full = {key: [np.full(p.numel, np.nan, np.float32) for p in self.params] for key in ("master", "m", "v")}
+        for L, A in zip(self.layouts, self.arenas):
+            n = L.state_numel
+            ex = [torch.empty(max(n, 1), dtype=torch.float32, device="cuda") for _ in range(3)]
+            self.D.dopt_state_export(L, A.bufs, *ex, A.workspace, self.stream)
+            export_to_model(L, len(self.params), tuple(e[:n].cpu().numpy() for e in ex), full)
+        return full
+
+    def model_params(self):
+        full = [np.zeros(p.numel, NP_STORE[p.param_dtype]) for p in self.params]
+        for L, A in zip(self.layouts, self.arenas):
+            host = [to_bits(b["param"].cpu()) for b in A.bufs]
+            for p, k, a, lo, hi, _ in shard_pieces(L, len(self.params)):
+                full[p][lo:hi] = host[k][a:a + hi - lo]
+        return full
+
+    def scalars(self):
+        s = self.D.dopt_state_scalars_get(self.layouts[0], self.arenas[0].workspace, self.stream)
+        return {"t": s["step_count"], "scale": s["loss_scale"], "growth_tracker": s["growth_tracker"],
+                "hysteresis_tracker": s["hysteresis_tracker"]}
+
+    def load(self, full, scalars):
+        sc = {"step_count": scalars["t"], "loss_scale": scalars["scale"],
+              "growth_tracker": scalars["growth_tracker"], "hysteresis_tracker": scalars["hysteresis_tracker"]}
+        for L, A in zip(self.layouts, self.arenas):
+            ex = [torch.from_numpy(e).to("cuda") if e.size else torch.zeros(1, device="cuda")
+                  for e in model_to_export(L, len(self.params), full)]
+            self.D.dopt_state_import(L, A.bufs, *ex, A.workspace, self.stream)
+            self.D.dopt_state_scalars_set(L, A.workspace, sc, self.stream)
+        torch.cuda.synchronize()
+
+
+def check_model_state(name, dev, ref):
+    out = {}
+    for key in ("master", "m", "v"):
+        out[key] = check_f32(f"{name} {key}", np.concatenate(dev[key]), np.concatenate(ref[key]))
+    return out
+
+
+def check_model_params(name, params, dev, ref):
+    out = {}
+    for p, x, y in zip(params, dev, ref):
+        out[p.name] = check_param(f"{name} param {p.name}", x, y, p.param_dtype)["max_ulp"]
+    return out

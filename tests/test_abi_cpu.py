@@ -11,6 +11,7 @@ import pytest
 import oracle
 from synth import PARAM_LISTS, WORKLOADS
 from synth.models import ParamSpec
+from tests.oracle_harness import shard_pieces
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -61,6 +62,11 @@ def _compare(params, N, r, bucket_size, busbw=0):
         if x["has_shard"]:
             for key in ("gbuf_world", "gbuf_world_in_bucket", "gbuf_local", "param"):
                 assert x[key] == y[key], (p, key)
+        else:
+            assert x["export_offset"] == -1
+    # model-space export offsets: the oracle's shards in model order, back to back
+    for p, _, _, _, _, xoff in shard_pieces(B, len(params)):
+        assert A.param(p)["export_offset"] == xoff, p
     for kind in oracle.GROUP_KINDS:
         for h in range(3):
             assert A.group(kind, h) == B.group(kind, h)
