@@ -32,12 +32,18 @@ constexpr int64_t kStreamingReadBytes = int64_t(192) << 20;
 // per wave for a pass that only reads).
 constexpr int kStatsUnroll = 4;
 
-// Tile descriptor: the param segments that overlap the tile.
-constexpr int32_t kTileFull = 1 << 30;   // the tile lies inside one segment
-constexpr int32_t kTileCountMask = kTileFull - 1;
+// Tile descriptor: the param segments that overlap the tile.  seg_count
+// holds the number of overlapping segments in its low 24 bits; when one
+// segment covers the whole tile, kTileFull is set and bits 24-28 hold that
+// segment's hyper-group (so the full-tile path needs no segment lookup).
+constexpr int32_t kTileFull = 1 << 30;
+constexpr int kTileHgShift = 24;
+constexpr int32_t kTileHgMask = 0x1f;
+constexpr int32_t kTileCountMask = (1 << kTileHgShift) - 1;
+static_assert(DOPT_MAX_HGROUPS <= kTileHgMask + 1, "hyper-group field too narrow");
 struct TileDesc {
     int32_t seg_first;
-    int32_t seg_count;  // number of overlapping segments | kTileFull
+    int32_t seg_count;
 };
 
 // Pre-communication check of whole buckets: a check tile is kCheckTile

@@ -132,7 +132,8 @@ static void build_tiles(Buffer &B) {
         while (j < ns && B.segs[j].start < hi) ++j;
         const int32_t cnt = static_cast<int32_t>(j - s);
         const bool full = cnt == 1 && B.segs[s].start <= lo && B.segs[s].end >= hi;
-        B.tiles[t] = TileDesc{static_cast<int32_t>(s), cnt | (full ? kTileFull : 0)};
+        const int32_t flags = full ? (kTileFull | (B.segs[s].hgroup << kTileHgShift)) : 0;
+        B.tiles[t] = TileDesc{static_cast<int32_t>(s), cnt | flags};
     }
     const int64_t stats_one_pass = (n_tiles + kStatsUnroll - 1) / kStatsUnroll;
     B.stats_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? stats_one_pass

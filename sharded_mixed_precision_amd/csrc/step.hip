@@ -83,16 +83,30 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
 template <int DT>
 struct Elem;
 
+// The raw bytes of 8 consecutive elements (16-bit types use `lo` only).
+// Kernels load raw packets first and convert after a scheduling barrier, so
+// that all of a batch's loads are in flight before the first one is waited
+// for.
+struct Raw8 {
+    u32x4 lo, hi;
+};
+
 template <>
 struct Elem<DOPT_BF16> {
     template <bool NT = false>
-    static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
-        const u32x4 u = ld16<NT>(static_cast<const uint16_t *>(base) + i);
+    static __device__ __forceinline__ Raw8 load_raw(const void *base, int64_t i) {
+        return Raw8{ld16<NT>(static_cast<const uint16_t *>(base) + i), u32x4{0, 0, 0, 0}};
+    }
+    static __device__ __forceinline__ void unpack(const Raw8 &r, float (&x)[kVec]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = __uint_as_float(u[j] << 16);
-            x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+            x[2 * j] = __uint_as_float(r.lo[j] << 16);
+            x[2 * j + 1] = __uint_as_float(r.lo[j] & 0xffff0000u);
         }
+    }
+    template <bool NT = false>
+    static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
+        unpack(load_raw<NT>(base, i), x);
     }
     static __device__ __forceinline__ uint32_t bits(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -116,13 +130,19 @@ struct Elem<DOPT_F16> {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
     }
     template <bool NT = false>
-    static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
-        const u32x4 u = ld16<NT>(static_cast<const uint16_t *>(base) + i);
+    static __device__ __forceinline__ Raw8 load_raw(const void *base, int64_t i) {
+        return Raw8{ld16<NT>(static_cast<const uint16_t *>(base) + i), u32x4{0, 0, 0, 0}};
+    }
+    static __device__ __forceinline__ void unpack(const Raw8 &r, float (&x)[kVec]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = up(u[j] & 0xffffu);
-            x[2 * j + 1] = up(u[j] >> 16);
+            x[2 * j] = up(r.lo[j] & 0xffffu);
+            x[2 * j + 1] = up(r.lo[j] >> 16);
         }
+    }
+    template <bool NT = false>
+    static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
+        unpack(load_raw<NT>(base, i), x);
     }
     static __device__ __forceinline__ uint32_t bits(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
@@ -159,6 +179,18 @@ __device__ __forceinline__ void store8f(float *base, int64_t i, const float (&x)
 template <>
 struct Elem<DOPT_F32> {
     template <bool NT = false>
+    static __device__ __forceinline__ Raw8 load_raw(const void *base, int64_t i) {
+        const float *f = static_cast<const float *>(base) + i;
+        return Raw8{ld16<NT>(f), ld16<NT>(f + 4)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw8 &r, float (&x)[kVec]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = __uint_as_float(r.lo[j]);
+            x[4 + j] = __uint_as_float(r.hi[j]);
+        }
+    }
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const void *base, int64_t i, float (&x)[kVec]) {
         load8f<NT>(static_cast<const float *>(base), i, x);
     }
@@ -174,6 +206,18 @@ __device__ __forceinline__ int owner_hgroup(const SegDesc *__restrict__ segs, in
     for (int32_t s = first; s < first + cnt; ++s)
         if (segs[s].start <= e && e < segs[s].end) return segs[s].hgroup;
     return -1;
+}
+
+// Bit j set when element i0 + j (i0 = this thread's first element of the
+// tile) belongs to a param.
+__device__ __forceinline__ uint32_t own_mask(const SegDesc *__restrict__ segs, const TileDesc &td, int64_t i0) {
+    if (td.seg_count & kTileFull) return 0xffu;
+    const int32_t cnt = td.seg_count & kTileCountMask;
+    uint32_t mk = 0;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+        if (owner_hgroup(segs, td.seg_first, cnt, i0 + j) >= 0) mk |= 1u << j;
+    return mk;
 }
 
 // ---- finalize: skip, norm, clip, loss scale, step count, AdamW scalars ------
@@ -303,38 +347,34 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
     const int64_t G = gridDim.x;
     for (int64_t t0 = blockIdx.x; t0 < n_tiles; t0 += kStatsUnroll * G) {
         TileDesc td[kStatsUnroll];
-        float g[kStatsUnroll][kVec];
+        Raw8 raw[kStatsUnroll];
+        // All kStatsUnroll loads are issued before any is waited for: a tile
+        // index past the end is clamped to the last tile (allocated arena
+        // memory) and its data ignored, so no load sits behind a branch.
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
             const int64_t t = t0 + u * G;
-            // the data load does not wait for the tile descriptor: every tile
-            // below n_tiles is allocated arena memory
-            const bool in = t < n_tiles;
-            td[u] = in ? tiles[t] : TileDesc{0, 0};
-            if (in) Elem<GD>::template load8<NT>(grad, t * kTile + int64_t(threadIdx.x) * kVec, g[u]);
+            const int64_t tl = t < n_tiles ? t : n_tiles - 1;
+            td[u] = tiles[tl];
+            raw[u] = Elem<GD>::template load_raw<NT>(grad, tl * kTile + int64_t(threadIdx.x) * kVec);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of the arithmetic
+        // The data are consumed without branching on them (an element that is
+        // not a shard element adds +0, which leaves the sum unchanged), so the
+        // compiler keeps every load ahead of the ownership tests.
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
-            const int32_t cnt = td[u].seg_count & kTileCountMask;
-            if (cnt == 0) continue;
-            if (td[u].seg_count & kTileFull) {
+            const int64_t i0 = (t0 + u * G) * kTile + int64_t(threadIdx.x) * kVec;
+            const uint32_t mk = t0 + u * G < n_tiles ? own_mask(segs, td[u], i0) : 0u;
+            float g[kVec];
+            Elem<GD>::unpack(raw[u], g);
 #pragma unroll
-                for (int j = 0; j < kVec; ++j) {
-                    const float x = g[u][j] * inv;
-                    const double xd = static_cast<double>(x);
-                    acc = fma(xd, xd, acc);
-                    zeros += (x == 0.0f) ? 1u : 0u;
-                }
-            } else {
-                const int64_t i0 = (t0 + u * G) * kTile + int64_t(threadIdx.x) * kVec;
-#pragma unroll
-                for (int j = 0; j < kVec; ++j) {
-                    if (owner_hgroup(segs, td[u].seg_first, cnt, i0 + j) < 0) continue;
-                    const float x = g[u][j] * inv;
-                    const double xd = static_cast<double>(x);
-                    acc = fma(xd, xd, acc);
-                    zeros += (x == 0.0f) ? 1u : 0u;
-                }
+            for (int j = 0; j < kVec; ++j) {
+                const bool own = (mk >> j) & 1u;
+                const float x = g[j] * inv;
+                const double xd = own ? static_cast<double>(x) : 0.0;
+                acc = fma(xd, xd, acc);
+                zeros += (own && x == 0.0f) ? 1u : 0u;
             }
         }
     }
@@ -375,17 +415,27 @@ __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict_
         float s[kVec];
 #pragma unroll
         for (int j = 0; j < kVec; ++j) s[j] = 0.0f;
-        for (int32_t c0 = 0; c0 < n_chunks; c0 += kReduceBatch) {
-            float x[kReduceBatch][kVec];
+        // full batches: all kReduceBatch loads issued before the first add
+        int32_t c0 = 0;
+        for (; c0 + kReduceBatch <= n_chunks; c0 += kReduceBatch) {
+            Raw8 raw[kReduceBatch];
 #pragma unroll
             for (int b = 0; b < kReduceBatch; ++b)
-                if (c0 + b < n_chunks) Elem<WD>::template load8<true>(chunks, int64_t(c0 + b) * stride + i0, x[b]);
+                raw[b] = Elem<WD>::template load_raw<true>(chunks, int64_t(c0 + b) * stride + i0);
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of the adds
 #pragma unroll
             for (int b = 0; b < kReduceBatch; ++b) {
-                if (c0 + b >= n_chunks) break;
+                float x[kVec];
+                Elem<WD>::unpack(raw[b], x);
 #pragma unroll
-                for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[b][j];
+                for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[j];
             }
+        }
+        for (; c0 < n_chunks; ++c0) {
+            float x[kVec];
+            Elem<WD>::template load8<true>(chunks, int64_t(c0) * stride + i0, x);
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) s[j] = s[j] + x[j];
         }
 #pragma unroll
         for (int j = 0; j < kVec; ++j) s[j] = s[j] * scale;
@@ -424,10 +474,11 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
             const int32_t i = i0 + j * kBlock;
-            q[j] = i < n ? part[i] : Partial{0.0, 0ull};
+            q[j] = part[i < n ? i : n - 1];
         }
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
+            if (i0 + j * kBlock >= n) break;
             a += q[j].sumsq;
             z += q[j].zeros;
         }
@@ -491,23 +542,29 @@ __global__ void __launch_bounds__(kBlock) k_check(const void *__restrict__ grad,
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
         const int64_t base = ct[t].start;
         const int64_t end = ct[t].end;
-        float g[kCheckLoads][kVec];
+        Raw8 raw[kCheckLoads];
+        // Loads past the bucket end are clamped to its last 8 elements (the
+        // bucket holds at least 128 elements from the tile start, and its end
+        // is a multiple of 128) and their values ignored, so all loads are
+        // issued before any is waited for.
 #pragma unroll
         for (int u = 0; u < kCheckLoads; ++u) {
             const int64_t i = base + u * kTile + int64_t(threadIdx.x) * kVec;
-            if (i < end) Elem<GD>::template load8<true>(grad, i, g[u]);
+            raw[u] = Elem<GD>::template load_raw<true>(grad, i < end ? i : end - kVec);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of the arithmetic
         double acc = 0.0;
         float mx = 0.0f;
 #pragma unroll
         for (int u = 0; u < kCheckLoads; ++u) {
-            const int64_t i = base + u * kTile + int64_t(threadIdx.x) * kVec;
-            if (i >= end) continue;
+            const bool in = base + u * kTile + int64_t(threadIdx.x) * kVec < end;
+            float g[kVec];
+            Elem<GD>::unpack(raw[u], g);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const double xd = static_cast<double>(g[u][j]);
+                const double xd = in ? static_cast<double>(g[j]) : 0.0;  // +0 leaves the sum unchanged
                 acc = fma(xd, xd, acc);
-                mx = fmaxf(mx, fabsf(g[u][j]));
+                mx = fmaxf(mx, in ? fabsf(g[j]) : 0.0f);
             }
         }
 #pragma unroll
@@ -550,10 +607,11 @@ __global__ void __launch_bounds__(kBlock) k_check_finish(const CheckPartial *__r
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
             const int64_t i = i0 + int64_t(j) * kBlock;
-            q[j] = i < t1 ? part[i] : CheckPartial{0.0, 0.0f, 0.0f};
+            q[j] = part[i < t1 ? i : t1 - 1];
         }
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
+            if (i0 + int64_t(j) * kBlock >= t1) break;
             a += q[j].sumsq;
             m = fmaxf(m, q[j].max_abs);
         }
@@ -625,15 +683,15 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
                                                  float *__restrict__ v, const TileDesc *__restrict__ tiles,
                                                  const SegDesc *__restrict__ segs, int64_t n_tiles,
                                                  const StepRec *__restrict__ rec) {
-    if (rec->skip) return;
     const float inv = rec->inv_scale;
     const int clip_on = rec->clip_on;
     const float clip = rec->clip;
     float *__restrict__ pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        // descriptor and data loads are issued together (arena memory is
-        // allocated for every tile); a tile with no param element goes
-        // through the per-element path and stores nothing
+        // the skip flag, the descriptor and the data loads are all issued
+        // before any of them is waited for (arena memory is allocated for
+        // every tile); a tile with no param element goes through the
+        // per-element path and stores nothing
         const TileDesc td = tiles[t];
         const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
         float g[kVec], p[kVec], a[kVec], b[kVec];
@@ -641,9 +699,12 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
         load8f(pm, i0, p);
         load8f(m, i0, a);
         load8f(v, i0, b);
+        // an atomic read cannot be hoisted out of the loop, so the data
+        // loads above do not wait for it
+        if (__hip_atomic_load(&rec->skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (td.seg_count & kTileFull) {
-            const Hp h = load_hp(rec, segs[td.seg_first].hgroup);
+            const Hp h = load_hp(rec, (td.seg_count >> kTileHgShift) & kTileHgMask);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) adamw(g[j], p[j], a[j], b[j], inv, clip_on, clip, h);
             store8f(pm, i0, p);
@@ -684,6 +745,36 @@ __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param,
         const TileDesc td = tiles[t];
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (cnt == 0) continue;
+        if (td.seg_count & kTileFull) {
+            // one segment covers the tile: export slot = arena slot + dx; all
+            // 24 loads are issued before the first store
+            const int64_t dx = segs[td.seg_first].xoff - segs[td.seg_first].start;
+            const int64_t e0 = t * kTile + threadIdx.x;
+            float a[kVec], b[kVec], c[kVec];
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t e = e0 + int64_t(j) * kBlock;
+                a[j] = IMPORT ? xm[e + dx] : pm[e];
+                b[j] = IMPORT ? xa[e + dx] : m[e];
+                c[j] = IMPORT ? xv[e + dx] : v[e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t e = e0 + int64_t(j) * kBlock;
+                if (IMPORT) {
+                    pm[e] = a[j];
+                    m[e] = b[j];
+                    v[e] = c[j];
+                    if (PD != DOPT_F32) Elem<PD>::store1(param, e, a[j]);
+                } else {
+                    xm[e + dx] = a[j];
+                    xa[e + dx] = b[j];
+                    xv[e + dx] = c[j];
+                }
+            }
+            continue;
+        }
         for (int j = 0; j < kVec; ++j) {
             const int64_t e = t * kTile + int64_t(j) * kBlock + threadIdx.x;
             int32_t s = td.seg_first;
