@@ -265,6 +265,10 @@ def main():
                          "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare); check: the whole-bucket "
                          "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads); checkpoint: the "
                          "model-space export and import of the rank's optimizer state (dopt_state_export / _import)")
+    ap.add_argument("--flush-llc", action="store_true",
+                    help="step mode: write a 512 MiB buffer before each timed step, so that no step data is left in "
+                         "the 256 MB last-level cache; each step is then timed on its own with HIP events and "
+                         "ms_per_step is their mean")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the step: copy an fp32 buffer of this many MiB (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -345,12 +349,24 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        step(ev_a[i], ev_b[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    if args.flush_llc:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        for i in range(K):
+            flush.fill_(i & 0xff)
+            ev_s[i].record(stream)
+            step(ev_a[i], ev_b[i])
+            ev_e[i].record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(a.elapsed_time(b) for a, b in zip(ev_s, ev_e))
+    else:
+        t_start.record(stream)
+        for i in range(K):
+            step(ev_a[i], ev_b[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
     apply_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / K
     st = D.dopt_read_stats(L, A.workspace, stream)
     assert st["skipped"] == 0 and st["step_count"] == args.warmup + K, st
@@ -375,7 +391,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {len(params)}-param list, rank {w.dp_rank} of N={w.dp_size}, "
                                f"bucket {w.bucket_size}, {E} shard elements",
-                   "shard_elements": E, "bytes_per_step": bytes_step},
+                   "shard_elements": E, "bytes_per_step": bytes_step,
+                   "llc": "flushed before each step" if args.flush_llc else "warm (steps back to back)"},
         "hbm_GBps_step": round(gbps, 1),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),

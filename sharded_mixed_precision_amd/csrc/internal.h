@@ -21,9 +21,13 @@ static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile si
 // or per kStatsUnroll tiles (pass 1), so no workgroup does more iterations
 // than another; large ones a fixed grid, grid-stride over the tiles.  The
 // grid is a function of the layout only, so the reduction order, and hence
-// the sum of squares, does not depend on the device it runs on.
+// the sum of squares, does not depend on the device it runs on.  The large-
+// window grids were chosen by measurement on MI355X: fewer workgroups than
+// the chip could hold keep fewer DRAM rows open at a time, which the
+// read-modify-write and copy passes preferred.
 constexpr int kStatsMaxBlocks = 1024;
-constexpr int kApplyMaxBlocks = 2048;
+constexpr int kApplyMaxBlocks = 512;
+constexpr int kCopyMaxBlocks = 256;  // state export / import
 constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which pass 2 uses one workgroup per tile
 // Grad windows above this size are streamed through pass 1 with
 // nontemporal loads (the MI355X last-level cache is 256 MB).
@@ -90,7 +94,7 @@ struct Buffer {
     int64_t numel = 0, unpadded = 0, window_numel = 0, arena_numel = 0, shard_numel = 0;
     std::vector<SegDesc> segs;
     std::vector<TileDesc> tiles;
-    int32_t stats_grid = 0, apply_grid = 0;
+    int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0;
     int32_t partial_base = 0;
     int64_t ws_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
     std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads

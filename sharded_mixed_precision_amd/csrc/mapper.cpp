@@ -140,6 +140,8 @@ static void build_tiles(Buffer &B) {
                                                                    : std::min<int64_t>(stats_one_pass, kStatsMaxBlocks));
     B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
+    B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
+                                                                  : std::min<int64_t>(n_tiles, kCopyMaxBlocks));
 }
 
 static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg, dopt_layout &L) {

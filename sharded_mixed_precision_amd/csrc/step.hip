@@ -386,9 +386,12 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 // [DP] §3.2 (reduce_scatter_with_fp32_accumulation): the N chunks this rank
 // received for each arena slot are added in fp32 in chunk order, starting
 // from +0, scaled once, stored in the grad dtype, and the stored value goes
-// through pass 1 exactly as in k_stats.  Chunk loads are issued kReduceBatch
-// at a time (the adds stay in chunk order); the chunks are read once, so
-// they are loaded nontemporally.
+// through pass 1 exactly as in k_stats.  Chunk loads are issued BATCH at a
+// time (the adds stay in chunk order); the chunks are read once, so they are
+// loaded nontemporally.  Small windows take BATCH = kReduceBatch (latency
+// bound: the more loads in flight per thread, the better); large ones
+// BATCH = 1, which measured faster on MI355X once the whole chip is busy
+// (fewer distinct DRAM rows open at a time).
 constexpr int kReduceBatch = 8;
 
 template <int GD>
@@ -400,7 +403,7 @@ __device__ __forceinline__ float stored_value<DOPT_BF16>(float x) { return __uin
 template <>
 __device__ __forceinline__ float stored_value<DOPT_F16>(float x) { return Elem<DOPT_F16>::up(Elem<DOPT_F16>::bits(x)); }
 
-template <int WD, int GD>
+template <int WD, int GD, int BATCH>
 __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict__ chunks, int64_t stride,
                                                         int32_t n_chunks, float scale, void *__restrict__ grad,
                                                         const TileDesc *__restrict__ tiles,
@@ -415,16 +418,16 @@ __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict_
         float s[kVec];
 #pragma unroll
         for (int j = 0; j < kVec; ++j) s[j] = 0.0f;
-        // full batches: all kReduceBatch loads issued before the first add
+        // full batches: all BATCH loads issued before the first add
         int32_t c0 = 0;
-        for (; c0 + kReduceBatch <= n_chunks; c0 += kReduceBatch) {
-            Raw8 raw[kReduceBatch];
+        for (; c0 + BATCH <= n_chunks; c0 += BATCH) {
+            Raw8 raw[BATCH];
 #pragma unroll
-            for (int b = 0; b < kReduceBatch; ++b)
+            for (int b = 0; b < BATCH; ++b)
                 raw[b] = Elem<WD>::template load_raw<true>(chunks, int64_t(c0 + b) * stride + i0);
             __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of the adds
 #pragma unroll
-            for (int b = 0; b < kReduceBatch; ++b) {
+            for (int b = 0; b < BATCH; ++b) {
                 float x[kVec];
                 Elem<WD>::unpack(raw[b], x);
 #pragma unroll
@@ -952,7 +955,11 @@ template <int WD, int GD>
 static void launch_reduce_dt(dim3 grid, hipStream_t s, const void *chunks, int64_t stride, int32_t n, float scale,
                              void *grad, const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles,
                              const DevState *st, Partial *out) {
-    k_reduce_stats<WD, GD><<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+    if (n_tiles <= kOneTileGridMax)
+        k_reduce_stats<WD, GD, kReduceBatch>
+            <<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+    else
+        k_reduce_stats<WD, GD, 1><<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
 }
 
 template <int WD>
@@ -1008,7 +1015,7 @@ static int state_copy(const dopt_layout *L, const dopt_buffer_tensors *bufs, flo
         const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
         const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
         const int64_t n_tiles = B.arena_numel / kTile;
-        const dim3 grid(B.apply_grid);
+        const dim3 grid(B.copy_grid);
         const dopt_buffer_tensors &b = bufs[k];
         if (B.pd == DOPT_BF16)
             k_state_copy<DOPT_BF16, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, b.master, b.exp_avg, b.exp_avg_sq,

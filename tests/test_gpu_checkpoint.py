@@ -138,3 +138,31 @@ def test_reshard_8_to_4_to_3_matches_one_rank(scaler, max_norm, inf_at):
         H.log(f"[reshard] N={n} after step {s}: {rep} param ulps {ulps}")
     if inf_at is not None:
         assert sc["scale"] == 512.0 and sc["t"] == s - 1
+
+
+def test_export_import_large_window_matches_oracle():
+    """A window of more than 8192 tiles takes the fixed-grid, grid-stride path."""
+    params = [ParamSpec("big", 20_000_003, "bf16", "bf16"), ParamSpec("n", 5000, "f32", "f32", 0, 1),
+              ParamSpec("h", 777, "bf16", "bf16", 1, 0)]
+    w = [synth.fill_normal(p.param_dtype, p.numel, 5, synth.weight_stream(i), 0, 0.02) for i, p in enumerate(params)]
+    g = [synth.fill_normal(p.grad_dtype, p.numel, 5, synth.grad_stream(i), 1, 1e-2) for i, p in enumerate(params)]
+    ranks = H.DeviceRanks(params, 1, 0)
+    ranks.init(w)
+    ranks.step(g, HPS, 1.0)
+    L, A = ranks.layouts[0], ranks.arenas[0]
+    assert L.buffer(0)["arena_numel"] // 2048 > 8192
+    run = OracleRun(params, 1, 0, 0, arena_numel=[A.info[k]["n"] for k in range(L.num_buffers)])
+    _oracle_view(run, ranks, 0)
+    n = L.state_numel
+    ex = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ranks.D.dopt_state_export(L, A.bufs, *ex, A.workspace, ranks.stream)
+    for e, x in zip(ex, oracle_export(run)):
+        assert np.array_equal(e.cpu().numpy().view(np.uint32), x.view(np.uint32))
+    rng = np.random.default_rng(9)
+    new = tuple((rng.standard_normal(n) * s).astype(np.float32) for s in (0.05, 1e-3, 1e-6))
+    ranks.D.dopt_state_import(L, A.bufs, *[torch.from_numpy(e).cuda() for e in new], A.workspace, ranks.stream)
+    oracle_import(run, new)
+    for k, b in enumerate(run.bufs):
+        for key, dkey in (("param", "param"), ("master", "master"), ("m", "exp_avg"), ("v", "exp_avg_sq")):
+            if b[key] is not None:
+                assert np.array_equal(to_bits(A.bufs[k][dkey].cpu()).view(np.uint8), b[key].view(np.uint8)), (k, key)
