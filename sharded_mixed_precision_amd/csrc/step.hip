@@ -229,11 +229,14 @@ __device__ __forceinline__ uint32_t own_mask(const SegDesc *__restrict__ segs, c
 // growth_interval clean steps; AdamW scalars are computed in double and
 // rounded once to fp32.  Called by every thread of one workgroup: thread 0
 // takes the step decision, then thread h fills the scalars of hyper-group h.
-__device__ void finalize_block(double sumsq, double zeros, DevState *st, StepRec *sr, dopt_stats *out,
-                               const FinalizeArgs &a) {
+// `cur` is the caller's copy of *st, read at kernel start so that its load
+// overlaps the reduction; the new state is written to *st.
+__device__ void finalize_block(double sumsq, double zeros, const DevState &cur, DevState *st, StepRec *sr,
+                               dopt_stats *out, const FinalizeArgs &a) {
     __shared__ double s_t;
     __shared__ int s_skip;
     if (threadIdx.x == 0) {
+        DevState n = cur;
         const int found_inf = isfinite(sumsq) ? 0 : 1;
         const double norm = sqrt(sumsq);
         out->found_inf = found_inf;
@@ -242,29 +245,29 @@ __device__ void finalize_block(double sumsq, double zeros, DevState *st, StepRec
         out->sumsq = sumsq;
         out->grad_norm = norm;
         out->num_zeros = static_cast<uint64_t>(zeros);
-        out->loss_scale_used = st->scale;
+        out->loss_scale_used = n.scale;
         sr->skip = found_inf;
-        sr->inv_scale = st->inv_scale;
-        if (st->kind == DOPT_SCALER_DYNAMIC) {
+        sr->inv_scale = n.inv_scale;
+        if (n.kind == DOPT_SCALER_DYNAMIC) {
             if (found_inf) {
-                st->growth_tracker = 0;
-                st->hysteresis_tracker -= 1;
-                if (st->hysteresis_tracker <= 0) st->scale = fmax(st->scale * st->backoff_factor, st->min_scale);
+                n.growth_tracker = 0;
+                n.hysteresis_tracker -= 1;
+                if (n.hysteresis_tracker <= 0) n.scale = fmax(n.scale * n.backoff_factor, n.min_scale);
             } else {
-                st->growth_tracker += 1;
-                if (st->growth_tracker == st->growth_interval) {
-                    st->growth_tracker = 0;
-                    st->hysteresis_tracker = st->hysteresis;
-                    st->scale = st->scale * st->growth_factor;
+                n.growth_tracker += 1;
+                if (n.growth_tracker == n.growth_interval) {
+                    n.growth_tracker = 0;
+                    n.hysteresis_tracker = n.hysteresis;
+                    n.scale = n.scale * n.growth_factor;
                 }
             }
-            st->inv_scale = static_cast<float>(1.0 / st->scale);
+            n.inv_scale = static_cast<float>(1.0 / n.scale);
         }
-        out->loss_scale_next = st->scale;
+        out->loss_scale_next = n.scale;
         double clip = 1.0;
         int clip_on = 0;
         if (!found_inf) {
-            st->t += 1;
+            n.t += 1;
             if (a.max_norm > 0.0) {
                 clip = a.max_norm / (norm + 1e-6);
                 clip_on = clip < 1.0 ? 1 : 0;
@@ -274,8 +277,9 @@ __device__ void finalize_block(double sumsq, double zeros, DevState *st, StepRec
         out->clip_applied = clip_on;
         sr->clip_on = clip_on;
         sr->clip = clip_on ? static_cast<float>(clip) : 0.0f;
-        out->step_count = st->t;
-        s_t = static_cast<double>(st->t);
+        out->step_count = n.t;
+        *st = n;
+        s_t = static_cast<double>(n.t);
         s_skip = found_inf;
     }
     __syncthreads();
@@ -295,7 +299,8 @@ __device__ void finalize_block(double sumsq, double zeros, DevState *st, StepRec
 
 __global__ void __launch_bounds__(64) k_finalize(const Record *rec, DevState *st, StepRec *sr, dopt_stats *out,
                                                  FinalizeArgs a) {
-    finalize_block(rec->sumsq, rec->zeros, st, sr, out, a);
+    const DevState cur = *st;
+    finalize_block(rec->sumsq, rec->zeros, cur, st, sr, out, a);
 }
 
 // ---- pass 1: unscale, sum of squares, zero count -----------------------------
@@ -463,13 +468,14 @@ __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict_
 // ... in order (loads issued together, kFinishBatch at a time), each wave
 // folds its 64 lanes with a fixed butterfly, and thread 0 adds the four wave
 // sums in order.
-constexpr int kFinishBatch = 4;
+constexpr int kFinishBatch = 8;
 
 template <bool FINALIZE>
 __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ part, int32_t n,
                                                   Record *__restrict__ rec, DevState *__restrict__ st,
                                                   StepRec *__restrict__ sr, dopt_stats *__restrict__ out,
                                                   FinalizeArgs fa) {
+    const DevState cur = *st;  // loaded now, used after the reduction
     double a = 0.0;
     unsigned long long z = 0;
     for (int32_t i0 = threadIdx.x; i0 < n; i0 += kFinishBatch * kBlock) {
@@ -479,11 +485,12 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
             const int32_t i = i0 + j * kBlock;
             q[j] = part[i < n ? i : n - 1];
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first add
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
-            if (i0 + j * kBlock >= n) break;
-            a += q[j].sumsq;
-            z += q[j].zeros;
+            const bool in = i0 + j * kBlock < n;  // a clamped duplicate adds +0
+            a += in ? q[j].sumsq : 0.0;
+            z += in ? q[j].zeros : 0ull;
         }
     }
 #pragma unroll
@@ -514,7 +521,7 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
     }
     if (FINALIZE) {
         __syncthreads();
-        finalize_block(s_tot[0], s_tot[1], st, sr, out, fa);
+        finalize_block(s_tot[0], s_tot[1], cur, st, sr, out, fa);
     }
 }
 
@@ -612,11 +619,12 @@ __global__ void __launch_bounds__(kBlock) k_check_finish(const CheckPartial *__r
             const int64_t i = i0 + int64_t(j) * kBlock;
             q[j] = part[i < t1 ? i : t1 - 1];
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first add
 #pragma unroll
         for (int j = 0; j < kFinishBatch; ++j) {
-            if (i0 + int64_t(j) * kBlock >= t1) break;
-            a += q[j].sumsq;
-            m = fmaxf(m, q[j].max_abs);
+            const bool in = i0 + int64_t(j) * kBlock < t1;  // a clamped duplicate adds +0
+            a += in ? q[j].sumsq : 0.0;
+            m = fmaxf(m, in ? q[j].max_abs : 0.0f);
         }
     }
 #pragma unroll
