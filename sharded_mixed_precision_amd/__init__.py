@@ -308,8 +308,8 @@ def dopt_init_state(layout: Layout, bufs: Sequence[Dict], scaler: dopt_scaler_cf
 def dopt_step(layout: Layout, bufs, hparams: Sequence, max_grad_norm: float, workspace, stream=None,
               want_stats: bool = True, _tensors_cache=None):
     st = dopt_stats() if want_stats else None
-    t = _tensors_cache if _tensors_cache is not None else _tensors(bufs)
-    hp = _hparams(hparams)
+    t = _tensors_cache if _tensors_cache is not None else (bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs))
+    hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
     _check(_lib.dopt_step(layout.handle, t, hp, len(hparams), max_grad_norm, _addr(workspace), _stream(stream),
                           ctypes.byref(st) if st is not None else None))
     return st.as_dict() if st is not None else None
