@@ -50,6 +50,17 @@ struct TileDesc {
     int32_t seg_count;
 };
 
+// Pass 2's boundary bitmap, passed by value: for a buffer of at most
+// kBitmapTiles tiles whose shards are all in one hyper-group `hg`, bit t is
+// set when tile t is not fully covered by one param's shard; a tile whose bit
+// is clear is then known to be full without a descriptor load.  on == 0: no
+// bitmap (read every tile's descriptor).
+constexpr int kBitmapTiles = 8192;
+struct TileBits {
+    int32_t on, hg;
+    uint32_t w[kBitmapTiles / 32];
+};
+
 // Pre-communication check of whole buckets: a check tile is kCheckTile
 // elements from the bucket start (bucket sizes are multiples of 128
 // elements, so an 8-element vector is either wholly inside a bucket or past
@@ -94,9 +105,15 @@ struct Buffer {
     int64_t numel = 0, unpadded = 0, window_numel = 0, arena_numel = 0, shard_numel = 0;
     std::vector<SegDesc> segs;
     std::vector<TileDesc> tiles;
+    // pass 1's copy of the tile table, in the order its workgroups read it:
+    // group q = k*G + b (workgroup b, k-th iteration, G = stats_grid) holds
+    // the descriptors of tiles b + k*G*kStatsUnroll + u*G, u < kStatsUnroll
+    // (empty descriptors past the last tile)
+    std::vector<TileDesc> stats_tiles;
+    TileBits bits{0, 0, {}};
     int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0;
     int32_t partial_base = 0;
-    int64_t ws_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
+    int64_t ws_tiles = 0, ws_stats_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
     std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads
     std::vector<CheckTile> chk_tile;    // per check tile
     int64_t chk_tiles = 0;

@@ -4,6 +4,7 @@
 // [ZL] "02 · ZeRO 显存账本与 Megatron DistributedOptimizer";
 // [DP] "Megatron-LM distributed 包深度解析：DDP 梯度同步与 finalize_model_grads 全流程".
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -138,6 +139,26 @@ static void build_tiles(Buffer &B) {
     const int64_t stats_one_pass = (n_tiles + kStatsUnroll - 1) / kStatsUnroll;
     B.stats_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? stats_one_pass
                                                                    : std::min<int64_t>(stats_one_pass, kStatsMaxBlocks));
+    // pass 2's boundary bitmap (see TileBits)
+    B.bits.on = 0;
+    B.bits.hg = 0;
+    std::fill(std::begin(B.bits.w), std::end(B.bits.w), 0u);
+    bool one_hg = true;
+    for (const SegDesc &sg : B.segs) one_hg = one_hg && sg.hgroup == B.segs.front().hgroup;
+    if (one_hg && n_tiles <= kBitmapTiles) {
+        B.bits.on = 1;
+        B.bits.hg = B.segs.empty() ? 0 : B.segs.front().hgroup;
+        for (int64_t t = 0; t < n_tiles; ++t)
+            if (!(B.tiles[t].seg_count & kTileFull)) B.bits.w[t >> 5] |= 1u << (t & 31);
+    }
+    const int64_t G = B.stats_grid, per_iter = G * kStatsUnroll;
+    const int64_t n_groups = (n_tiles + per_iter - 1) / per_iter * G;
+    B.stats_tiles.assign(static_cast<size_t>(n_groups * kStatsUnroll), TileDesc{0, 0});
+    for (int64_t q = 0; q < n_groups; ++q)
+        for (int64_t u = 0; u < kStatsUnroll; ++u) {
+            const int64_t t = q % G + (q / G) * per_iter + u * G;
+            if (t < n_tiles) B.stats_tiles[static_cast<size_t>(q * kStatsUnroll + u)] = B.tiles[static_cast<size_t>(t)];
+        }
     B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
@@ -199,6 +220,8 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
     for (Buffer &B : L.buffers) {
         B.ws_tiles = ws;
         ws += align_up(int64_t(B.tiles.size()) * int64_t(sizeof(TileDesc)), 256);
+        B.ws_stats_tiles = ws;
+        ws += align_up(int64_t(B.stats_tiles.size()) * int64_t(sizeof(TileDesc)), 256);
         B.ws_segs = ws;
         ws += align_up(std::max<int64_t>(int64_t(B.segs.size()), 1) * int64_t(sizeof(SegDesc)), 256);
         // whole-bucket check: the bucket table and one 16-byte partial per check tile

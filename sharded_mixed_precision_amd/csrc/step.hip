@@ -342,35 +342,65 @@ __device__ __forceinline__ void block_sum_store(double acc, unsigned long long z
     }
 }
 
+// A workgroup's k-th batch is tiles b + k*G*kStatsUnroll + u*G (b = block,
+// G = grid size, u < kStatsUnroll).  Its descriptors come from pass 1's copy
+// of the tile table (`groups`), where they are consecutive, so each wave
+// reads them with one scalar load: with one load per tile, the scalar-cache
+// misses of the ~2000 workgroups of a small window cost MI355X about 3 us.
+struct TileGroup {
+    TileDesc d[kStatsUnroll];
+};
+
 template <int GD, bool NT>
-__global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad, const TileDesc *__restrict__ tiles,
+__global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad, const TileGroup *__restrict__ groups,
                                                  const SegDesc *__restrict__ segs, int64_t n_tiles,
                                                  const DevState *__restrict__ st, Partial *__restrict__ out) {
     const float inv = st->inv_scale;
     double acc = 0.0;
     uint32_t zeros = 0;
     const int64_t G = gridDim.x;
-    for (int64_t t0 = blockIdx.x; t0 < n_tiles; t0 += kStatsUnroll * G) {
-        TileDesc td[kStatsUnroll];
+    int64_t q = blockIdx.x;
+    for (int64_t t0 = blockIdx.x; t0 < n_tiles; t0 += kStatsUnroll * G, q += G) {
         Raw8 raw[kStatsUnroll];
-        // All kStatsUnroll loads are issued before any is waited for: a tile
-        // index past the end is clamped to the last tile (allocated arena
-        // memory) and its data ignored, so no load sits behind a branch.
+        // All loads are issued before any is waited for: a tile index past
+        // the end is clamped to the last tile (allocated arena memory) and its
+        // data ignored (its descriptor is an empty one).
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
             const int64_t t = t0 + u * G;
             const int64_t tl = t < n_tiles ? t : n_tiles - 1;
-            td[u] = tiles[tl];
             raw[u] = Elem<GD>::template load_raw<NT>(grad, tl * kTile + int64_t(threadIdx.x) * kVec);
         }
+        const TileGroup tg = groups[q];
         __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of the arithmetic
+        // Nearly every batch lies inside one param's shard: no ownership tests
+        // there (the descriptors are the same for every thread, so the branch
+        // does not diverge).
+        bool full = true;
+#pragma unroll
+        for (int u = 0; u < kStatsUnroll; ++u) full = full && (tg.d[u].seg_count & kTileFull) != 0;
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < kStatsUnroll; ++u) {
+                float g[kVec];
+                Elem<GD>::unpack(raw[u], g);
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) {
+                    const float x = g[j] * inv;
+                    const double xd = static_cast<double>(x);
+                    acc = fma(xd, xd, acc);
+                    zeros += x == 0.0f ? 1u : 0u;
+                }
+            }
+            continue;
+        }
         // The data are consumed without branching on them (an element that is
         // not a shard element adds +0, which leaves the sum unchanged), so the
         // compiler keeps every load ahead of the ownership tests.
 #pragma unroll
         for (int u = 0; u < kStatsUnroll; ++u) {
             const int64_t i0 = (t0 + u * G) * kTile + int64_t(threadIdx.x) * kVec;
-            const uint32_t mk = t0 + u * G < n_tiles ? own_mask(segs, td[u], i0) : 0u;
+            const uint32_t mk = t0 + u * G < n_tiles ? own_mask(segs, tg.d[u], i0) : 0u;
             float g[kVec];
             Elem<GD>::unpack(raw[u], g);
 #pragma unroll
@@ -693,17 +723,22 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
                                                  float *__restrict__ master, float *__restrict__ m,
                                                  float *__restrict__ v, const TileDesc *__restrict__ tiles,
                                                  const SegDesc *__restrict__ segs, int64_t n_tiles,
-                                                 const StepRec *__restrict__ rec) {
+                                                 const StepRec *__restrict__ rec, TileBits tb) {
     const float inv = rec->inv_scale;
     const int clip_on = rec->clip_on;
     const float clip = rec->clip;
+    // One hyper-group's scalars (the bitmap's group, else group 0's) are
+    // loaded up front with the other step scalars, so a full tile of that
+    // group has no scalar load that waits for its descriptor.
+    const int hpre = tb.on ? tb.hg : 0;
+    const Hp h0 = load_hp(rec, hpre);
     float *__restrict__ pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        // the skip flag, the descriptor and the data loads are all issued
-        // before any of them is waited for (arena memory is allocated for
-        // every tile); a tile with no param element goes through the
-        // per-element path and stores nothing
-        const TileDesc td = tiles[t];
+        // the data loads, the skip flag and the descriptor (read only for a
+        // boundary tile, or when the buffer has no bitmap) are all issued before
+        // any of them is waited for (arena memory is allocated for every
+        // tile); a tile with no param element goes through the per-element
+        // path and stores nothing
         const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
         float g[kVec], p[kVec], a[kVec], b[kVec];
         Elem<GD>::load8(grad, i0, g);
@@ -712,10 +747,14 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
         load8f(v, i0, b);
         // an atomic read cannot be hoisted out of the loop, so the data
         // loads above do not wait for it
-        if (__hip_atomic_load(&rec->skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+        const int skip = __hip_atomic_load(&rec->skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        TileDesc td{0, kTileFull | (hpre << kTileHgShift)};
+        if (!tb.on || ((tb.w[t >> 5] >> (t & 31)) & 1u)) td = tiles[t];
+        if (skip) return;
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (td.seg_count & kTileFull) {
-            const Hp h = load_hp(rec, (td.seg_count >> kTileHgShift) & kTileHgMask);
+            const int hg = (td.seg_count >> kTileHgShift) & kTileHgMask;
+            const Hp h = hg == hpre ? h0 : load_hp(rec, hg);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) adamw(g[j], p[j], a[j], b[j], inv, clip_on, clip, h);
             store8f(pm, i0, p);
@@ -873,19 +912,19 @@ static int check_bufs(const dopt_layout *L, const dopt_buffer_tensors *bufs, con
 
 template <int PD>
 static void launch_apply_gd(int gd, dim3 grid, hipStream_t s, const dopt_buffer_tensors &b, const TileDesc *tiles,
-                            const SegDesc *segs, int64_t n_tiles, const StepRec *rec) {
+                            const SegDesc *segs, int64_t n_tiles, const StepRec *rec, const TileBits &tb) {
     switch (gd) {
     case DOPT_BF16:
         k_apply<PD, DOPT_BF16><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                     n_tiles, rec);
+                                                     n_tiles, rec, tb);
         break;
     case DOPT_F16:
         k_apply<PD, DOPT_F16><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                    n_tiles, rec);
+                                                    n_tiles, rec, tb);
         break;
     default:
         k_apply<PD, DOPT_F32><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                    n_tiles, rec);
+                                                    n_tiles, rec, tb);
         break;
     }
 }
@@ -929,7 +968,7 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
     Partial *part = reinterpret_cast<Partial *>(ws_ptr(ws, kWsPartials));
     for (size_t k = 0; k < L->buffers.size(); ++k) {
         const Buffer &B = L->buffers[k];
-        const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
+        const TileGroup *tiles = reinterpret_cast<const TileGroup *>(ws_ptr(ws, B.ws_stats_tiles));
         const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
         const int64_t n_tiles = B.arena_numel / kTile;
         const dim3 grid(B.stats_grid);
@@ -1060,6 +1099,10 @@ int dopt_init_state(const dopt_layout *L, const dopt_buffer_tensors *bufs, const
         rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_tiles), B.tiles.data(), B.tiles.size() * sizeof(TileDesc),
                                       hipMemcpyHostToDevice, stream),
                        "copy tile table");
+        if (rc) return rc;
+        rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_stats_tiles), B.stats_tiles.data(),
+                                      B.stats_tiles.size() * sizeof(TileDesc), hipMemcpyHostToDevice, stream),
+                       "copy pass-1 tile table");
         if (rc) return rc;
         if (!B.segs.empty()) {
             rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_segs), B.segs.data(), B.segs.size() * sizeof(SegDesc),
@@ -1241,13 +1284,13 @@ int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void 
         const dim3 grid(B.apply_grid);
         switch (B.pd) {
         case DOPT_BF16:
-            launch_apply_gd<DOPT_BF16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec);
+            launch_apply_gd<DOPT_BF16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         case DOPT_F16:
-            launch_apply_gd<DOPT_F16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec);
+            launch_apply_gd<DOPT_F16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         default:
-            launch_apply_gd<DOPT_F32>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec);
+            launch_apply_gd<DOPT_F32>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         }
         if ((rc = check_launch("launch k_apply"))) return rc;
