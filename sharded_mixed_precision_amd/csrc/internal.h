@@ -111,8 +111,8 @@ struct Buffer {
     // (empty descriptors past the last tile)
     std::vector<TileDesc> stats_tiles;
     TileBits bits{0, 0, {}};
-    int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0;
-    int32_t partial_base = 0;
+    int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0, reduce_grid = 0;
+    int32_t partial_base = 0, reduce_partial_base = 0;  // first partial slot of pass 1 / the fused reduce
     int64_t ws_tiles = 0, ws_stats_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
     std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads
     std::vector<CheckTile> chk_tile;    // per check tile
@@ -139,6 +139,6 @@ struct dopt_layout {
     std::vector<dopt::Param> params;
     std::vector<dopt::Buffer> buffers;
     int64_t state_numel = 0;
-    int32_t total_partials = 0;
+    int32_t total_partials = 0, total_reduce_partials = 0;
     int64_t ws_bytes = 0;
 };

@@ -159,6 +159,8 @@ static void build_tiles(Buffer &B) {
             const int64_t t = q % G + (q / G) * per_iter + u * G;
             if (t < n_tiles) B.stats_tiles[static_cast<size_t>(q * kStatsUnroll + u)] = B.tiles[static_cast<size_t>(t)];
         }
+    // the fused reduce + pass 1: one tile per workgroup on small windows
+    B.reduce_grid = n_tiles <= kOneTileGridMax ? static_cast<int32_t>(n_tiles) : B.stats_grid;
     B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
@@ -196,7 +198,7 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
         L.buffers[k].params.push_back(i);
     }
     int64_t ws = kWsPartials;
-    int32_t partials = 0;
+    int32_t partials = 0, reduce_partials = 0;
     for (Buffer &B : L.buffers) {
         int rc = lay_out_buffer(L, B, cfg->bucket_size, cfg->pad_for_high_busbw != 0);
         if (rc != DOPT_OK) return rc;
@@ -204,9 +206,12 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
         build_tiles(B);
         B.partial_base = partials;
         partials += B.stats_grid;
+        B.reduce_partial_base = reduce_partials;
+        reduce_partials += B.reduce_grid;
         L.state_numel += B.shard_numel;
     }
     L.total_partials = partials;
+    L.total_reduce_partials = reduce_partials;
     // model-space export: the shards in model order, back to back
     int64_t xoff = 0;
     for (Param &p : L.params) {
@@ -216,7 +221,7 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
     }
     for (Buffer &B : L.buffers)
         for (SegDesc &s : B.segs) s.xoff = L.params[s.param].xoff;
-    ws += align_up(int64_t(partials) * 16, 256);
+    ws += align_up(int64_t(std::max(partials, reduce_partials)) * 16, 256);
     for (Buffer &B : L.buffers) {
         B.ws_tiles = ws;
         ws += align_up(int64_t(B.tiles.size()) * int64_t(sizeof(TileDesc)), 256);

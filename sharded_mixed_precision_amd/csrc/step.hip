@@ -951,9 +951,9 @@ static int build_finalize_args(const dopt_layout *L, const dopt_hparams *hp, int
 // The fixed-order reduction of all pass-1 partials, and the finalize when
 // FINALIZE is set.
 template <bool FINALIZE>
-static int launch_finish(const dopt_layout *L, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
+static int launch_finish(int32_t n_partials, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
     k_finish<FINALIZE><<<1, kBlock, 0, stream>>>(reinterpret_cast<const Partial *>(ws_ptr(ws, kWsPartials)),
-                                                 L->total_partials, reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
+                                                 n_partials, reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
                                                  reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
                                                  reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
                                                  reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), fa);
@@ -995,7 +995,7 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
         int rc = check_launch("launch k_stats");
         if (rc) return rc;
     }
-    return launch_finish<FINALIZE>(L, ws, stream, fa);
+    return launch_finish<FINALIZE>(L->total_partials, ws, stream, fa);
 }
 
 template <int WD, int GD>
@@ -1032,8 +1032,8 @@ static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, 
         const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
         const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
         const int64_t n_tiles = B.arena_numel / kTile;
-        const dim3 grid(B.stats_grid);  // one partial per workgroup, as pass 1
-        Partial *out = part + B.partial_base;
+        const dim3 grid(B.reduce_grid);  // one partial per workgroup
+        Partial *out = part + B.reduce_partial_base;
         // the grad arena is this entry point's output (read-only everywhere else)
         void *grad_out = const_cast<void *>(bufs[k].grad);
         if (wd == DOPT_BF16)
@@ -1048,7 +1048,7 @@ static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, 
         int rc = check_launch("launch k_reduce_stats");
         if (rc) return rc;
     }
-    return launch_finish<FINALIZE>(L, ws, stream, fa);
+    return launch_finish<FINALIZE>(L->total_reduce_partials, ws, stream, fa);
 }
 
 template <bool IMPORT>
