@@ -75,6 +75,15 @@ def test_mixed_dtypes_hgroups_lone_buckets():
     H.run_full(H.Case("mixed", params, 3, 1, bucket_size=5000, steps=4, hparams=hps))
 
 
+def test_one_nonzero_hgroup_full_tiles():
+    """Every shard of the buffer in hyper-group 2, with tiles wholly inside one
+    shard: pass 2 takes such tiles' AdamW scalars from the group it loaded
+    up front, which must be group 2's (the three groups differ)."""
+    params = [ParamSpec("a", 50_000, "bf16", "bf16", 0, 2), ParamSpec("b", 30_011, "bf16", "bf16", 0, 2)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
+    H.run_full(H.Case("hgroup2", params, 2, 1, steps=3, hparams=hps))
+
+
 def test_high_busbw_padding():
     params = [ParamSpec("a", 100_000, "bf16", "bf16"), ParamSpec("b", 3000, "bf16", "bf16")]
     H.run_full(H.Case("busbw", params, 8, 6, busbw=1, steps=2))
