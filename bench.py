@@ -11,7 +11,9 @@ recorded inside it).  The launch duration of pass 2 for the roofline comes
 from K further steps, each running pass 2 APPLY_BATCH times back to back
 between two HIP events on the launch stream (the repeats apply the step's
 own scalars again: the same kernel, launch configuration and bytes), so the
-events' own cost is spread over the batch.
+events' own cost is spread over the batch.  Last, K steps run with the
+256 MB last-level cache flushed before each (`llc_flushed`): back-to-back
+steps of a small window find much of their data still in that cache.
 
 Prints one JSON line.  The default workload is a GPT-2-small-shaped param
 list sharded N=8, rank 3, 40M-element buckets, bf16 params and grads.
@@ -353,9 +355,12 @@ def main():
         step()
     torch.cuda.synchronize()
     K = args.steps
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_llc else None
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
-    if args.flush_llc:
+
+    def flushed_steps():
+        """K steps, each timed on its own right after a 512 MiB write that
+        leaves no step data in the 256 MB last-level cache; total ms."""
         ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         for i in range(K):
@@ -364,7 +369,10 @@ def main():
             step()
             ev_e[i].record(stream)
         torch.cuda.synchronize()
-        total_ms = sum(a.elapsed_time(b) for a, b in zip(ev_s, ev_e))
+        return sum(a.elapsed_time(b) for a, b in zip(ev_s, ev_e))
+
+    if args.flush_llc:
+        total_ms = flushed_steps()
     else:
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
@@ -378,13 +386,17 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for i in range(K):
-        if flush is not None:
+        if args.flush_llc:
             flush.fill_(i & 0xff)
         step_bracketed(ev_a[i], ev_b[i])
     torch.cuda.synchronize()
     apply_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / (K * APPLY_BATCH)
+    # the same steps with the last-level cache flushed before each (reported
+    # beside the back-to-back figure; a training step runs after forward and
+    # backward have passed far more than 256 MB through the cache)
+    flushed_ms = None if args.flush_llc else flushed_steps() / K
     st = D.dopt_read_stats(L, A.workspace, stream)
-    assert st["skipped"] == 0 and st["step_count"] == args.warmup + 2 * K, st
+    assert st["skipped"] == 0 and st["step_count"] == args.warmup + (2 if args.flush_llc else 3) * K, st
     ms = total_ms / K
     value = E / (ms * 1e-3) / 1e9
     gbps = bytes_step / (ms * 1e-3) / 1e9
@@ -415,6 +427,9 @@ def main():
                      "traffic": traffic, "launch_ms": round(apply_ms, 5), "launches_timed": K * APPLY_BATCH,
                      "algorithmic_bytes_per_launch": apply_bytes},
     }
+    if flushed_ms is not None:
+        out["llc_flushed"] = {"ms_per_step": round(flushed_ms, 5), "value": round(E / (flushed_ms * 1e-3) / 1e9, 3),
+                              "unit": "Gparams/s", "hbm_GBps_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
