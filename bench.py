@@ -128,6 +128,32 @@ def cpu_baseline(workload, seconds: float):
                       f"passes in {el:.1f}s, 1 thread"}
 
 
+def skip_step(L, A, step, K: int, stream):
+    """An overflow step: one grad element of the first shard set to +inf, so
+    pass 1 finds it and pass 2 writes nothing.  Timed over K steps with
+    nothing else in the timed region; the bytes are pass 1's (the grad)."""
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    p0 = next(L.param(p) for p in range(L.n_params) if L.param(p)["has_shard"])
+    A.bufs[p0["buffer"]]["grad"][p0["arena_offset"]] = float("inf")
+    step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    st = D.dopt_read_stats(L, A.workspace, stream)
+    assert st["skipped"] == 1 and st["found_inf"] == 1, st
+    ms = t0.elapsed_time(t1) / K
+    nbytes = sum(ES[info["gd"]] * info["shard_numel"] for info in A.info)
+    return {"ms_per_step": round(ms, 5), "bytes_per_step": nbytes, "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "steps": K}
+
+
 def bench_reduce(args, w, L, A, bufs_c, hp_c, stream):
     """The local half of a reduce-scatter with fp32 accumulation fused with
     pass 1: dp_size bf16 chunks per window slot are summed in fp32 and written
@@ -397,6 +423,7 @@ def main():
     flushed_ms = None if args.flush_llc else flushed_steps() / K
     st = D.dopt_read_stats(L, A.workspace, stream)
     assert st["skipped"] == 0 and st["step_count"] == args.warmup + (2 if args.flush_llc else 3) * K, st
+    skip = skip_step(L, A, step, K, stream) if w.dynamic_scale else None
     ms = total_ms / K
     value = E / (ms * 1e-3) / 1e9
     gbps = bytes_step / (ms * 1e-3) / 1e9
@@ -427,6 +454,8 @@ def main():
                      "traffic": traffic, "launch_ms": round(apply_ms, 5), "launches_timed": K * APPLY_BATCH,
                      "algorithmic_bytes_per_launch": apply_bytes},
     }
+    if skip is not None:
+        out["skip_step"] = skip
     if flushed_ms is not None:
         out["llc_flushed"] = {"ms_per_step": round(flushed_ms, 5), "value": round(E / (flushed_ms * 1e-3) / 1e9, 3),
                               "unit": "Gparams/s", "hbm_GBps_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9, 1)}

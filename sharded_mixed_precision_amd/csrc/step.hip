@@ -724,6 +724,7 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
                                                  float *__restrict__ v, const TileDesc *__restrict__ tiles,
                                                  const SegDesc *__restrict__ segs, int64_t n_tiles,
                                                  const StepRec *__restrict__ rec, TileBits tb) {
+    const int skip = rec->skip;
     const float inv = rec->inv_scale;
     const int clip_on = rec->clip_on;
     const float clip = rec->clip;
@@ -732,25 +733,24 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
     // group has no scalar load that waits for its descriptor.
     const int hpre = tb.on ? tb.hg : 0;
     const Hp h0 = load_hp(rec, hpre);
+    // A skipped step (overflow) touches no data.  The flag is loaded with
+    // the other step scalars, which the first data load waits for anyway.
+    if (skip) return;
     float *__restrict__ pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        // the data loads, the skip flag and the descriptor (read only for a
-        // boundary tile, or when the buffer has no bitmap) are all issued before
-        // any of them is waited for (arena memory is allocated for every
-        // tile); a tile with no param element goes through the per-element
-        // path and stores nothing
+        // the data loads and the descriptor (read only for a boundary tile,
+        // or when the buffer has no bitmap) are issued before either is
+        // waited for (arena memory is allocated for every tile); a tile with
+        // no param element goes through the per-element path and stores
+        // nothing
         const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
         float g[kVec], p[kVec], a[kVec], b[kVec];
         Elem<GD>::load8(grad, i0, g);
         load8f(pm, i0, p);
         load8f(m, i0, a);
         load8f(v, i0, b);
-        // an atomic read cannot be hoisted out of the loop, so the data
-        // loads above do not wait for it
-        const int skip = __hip_atomic_load(&rec->skip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         TileDesc td{0, kTileFull | (hpre << kTileHgShift)};
         if (!tb.on || ((tb.w[t >> 5] >> (t & 31)) & 1u)) td = tiles[t];
-        if (skip) return;
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (td.seg_count & kTileFull) {
             const int hg = (td.seg_count >> kTileHgShift) & kTileHgMask;
