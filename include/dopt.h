@@ -191,7 +191,8 @@ int dopt_layout_rank_window(const dopt_layout *layout, int32_t k, int32_t b, int
 int dopt_layout_param(const dopt_layout *layout, int64_t p, dopt_param_info *out);
 /* Model-order indices of the params of one group kind and hyper-group; writes
  * at most cap entries to idx (host, may be NULL) and returns the full count,
- * or a negative error code. */
+ * or a negative error code (DOPT_ERR_RANGE for a kind or hyper-group out of
+ * range). */
 int64_t dopt_layout_group(const dopt_layout *layout, int32_t kind, int32_t hgroup, int64_t *idx, int64_t cap);
 /* Param elements on this rank over all buffers (the optimizer-state length
  * of the ledger in [ZL] §2). */

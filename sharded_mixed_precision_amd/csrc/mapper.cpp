@@ -369,6 +369,7 @@ int dopt_layout_param(const dopt_layout *L, int64_t p, dopt_param_info *out) {
 int64_t dopt_layout_group(const dopt_layout *L, int32_t kind, int32_t hgroup, int64_t *idx, int64_t cap) {
     if (!L) return fail(DOPT_ERR_INVALID, "null layout");
     if (kind < DOPT_GROUP_MODEL_FLOAT16 || kind > DOPT_GROUP_SHARD_FP32) return fail(DOPT_ERR_RANGE, "group kind");
+    if (hgroup < 0 || hgroup >= DOPT_MAX_HGROUPS) return fail(DOPT_ERR_RANGE, "hyper-group");
     const bool lowp = kind == DOPT_GROUP_MODEL_FLOAT16 || kind == DOPT_GROUP_SHARD_FLOAT16 ||
                       kind == DOPT_GROUP_SHARD_FP32_FROM_FLOAT16;
     int64_t count = 0;
