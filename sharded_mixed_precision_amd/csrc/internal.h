@@ -17,18 +17,18 @@ constexpr int kVec = 8;
 constexpr int kTile = kBlock * kVec;
 static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile size");
 
-// Workgroups per launch.  Small windows get one workgroup per tile (pass 2)
-// or per kStatsUnroll tiles (pass 1), so no workgroup does more iterations
-// than another; large ones a fixed grid, grid-stride over the tiles.  The
-// grid is a function of the layout only, so the reduction order, and hence
-// the sum of squares, does not depend on the device it runs on.  The large-
-// window grids were chosen by measurement on MI355X: fewer workgroups than
-// the chip could hold keep fewer DRAM rows open at a time, which the
-// read-modify-write and copy passes preferred.
+// Workgroups per launch.  Small windows get one workgroup per tile (pass 2,
+// the fused reduce, the state copy) or per kStatsUnroll tiles (pass 1), so no
+// workgroup does more iterations than another; large ones a fixed grid,
+// grid-stride over the tiles.  The grid is a function of the layout only, so
+// the reduction order, and hence the sum of squares, does not depend on the
+// device it runs on.  The large-window grids were chosen by measurement on
+// MI355X: fewer workgroups than the chip could hold keep fewer DRAM rows open
+// at a time, which the read-modify-write and copy passes preferred.
 constexpr int kStatsMaxBlocks = 1024;
 constexpr int kApplyMaxBlocks = 512;
 constexpr int kCopyMaxBlocks = 256;  // state export / import
-constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which pass 2 uses one workgroup per tile
+constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which a window counts as small
 // Grad windows above this size are streamed through pass 1 with
 // nontemporal loads (the MI355X last-level cache is 256 MB).
 constexpr int64_t kStreamingReadBytes = int64_t(192) << 20;
