@@ -42,7 +42,7 @@ APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    "gpt2-small": {"src": "fdff4266f0b9f944", "bytes_per_launch": 440908942},
+    "gpt2-small": {"src": "358784de6b1411c9", "bytes_per_launch": 447039748},
 }
 
 
