@@ -80,6 +80,31 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *static_cast<const u32x4 *>(p);
 }
 
+// Tile-local buffer access (pass 2).  A resource descriptor covers one
+// 2048-element tile of one stream: the tile base is wave-uniform and sits in
+// scalar registers, so every stream of a tile shares one per-lane byte offset
+// instead of holding a 64-bit address per lane.  The descriptor is raw
+// (stride 0, range in bytes) with the 32-bit data format that untyped dword
+// accesses take on this ISA; an access past the range would read zero and
+// write nothing, and none is made.
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *tile_base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(tile_base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, int32_t off, u32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+}
+__device__ __forceinline__ float bld4(__amdgpu_buffer_rsrc_t r, int32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, int32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
 template <int DT>
 struct Elem;
 
@@ -93,6 +118,7 @@ struct Raw8 {
 
 template <>
 struct Elem<DOPT_BF16> {
+    static constexpr int64_t kBytes = 2;
     template <bool NT = false>
     static __device__ __forceinline__ Raw8 load_raw(const void *base, int64_t i) {
         return Raw8{ld16<NT>(static_cast<const uint16_t *>(base) + i), u32x4{0, 0, 0, 0}};
@@ -122,10 +148,29 @@ struct Elem<DOPT_BF16> {
     static __device__ __forceinline__ void store1(void *base, int64_t i, float x) {
         static_cast<uint16_t *>(base)[i] = static_cast<uint16_t>(bits(x));
     }
+    // lane's 8 elements of a tile through its resource descriptor
+    static __device__ __forceinline__ void bload8(__amdgpu_buffer_rsrc_t r, int32_t lane, float (&x)[kVec]) {
+        unpack(Raw8{bld16(r, lane * 16), u32x4{0, 0, 0, 0}}, x);
+    }
+    static __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j) {
+        return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, lane * 16 + j * 2, 0, 0)) << 16);
+    }
+    static __device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits(x)), r, lane * 16 + j * 2, 0, 0);
+    }
+    static __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int32_t lane, const float (&x)[kVec]) {
+        u32x4 u;
+        u[0] = bits(x[0]) | (bits(x[1]) << 16);
+        u[1] = bits(x[2]) | (bits(x[3]) << 16);
+        u[2] = bits(x[4]) | (bits(x[5]) << 16);
+        u[3] = bits(x[6]) | (bits(x[7]) << 16);
+        bst16(r, lane * 16, u);
+    }
 };
 
 template <>
 struct Elem<DOPT_F16> {
+    static constexpr int64_t kBytes = 2;
     static __device__ __forceinline__ float up(uint32_t h) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
     }
@@ -158,6 +203,24 @@ struct Elem<DOPT_F16> {
     static __device__ __forceinline__ void store1(void *base, int64_t i, float x) {
         static_cast<uint16_t *>(base)[i] = static_cast<uint16_t>(bits(x));
     }
+    // lane's 8 elements of a tile through its resource descriptor
+    static __device__ __forceinline__ void bload8(__amdgpu_buffer_rsrc_t r, int32_t lane, float (&x)[kVec]) {
+        unpack(Raw8{bld16(r, lane * 16), u32x4{0, 0, 0, 0}}, x);
+    }
+    static __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j) {
+        return up(__builtin_amdgcn_raw_buffer_load_b16(r, lane * 16 + j * 2, 0, 0));
+    }
+    static __device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bits(x)), r, lane * 16 + j * 2, 0, 0);
+    }
+    static __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int32_t lane, const float (&x)[kVec]) {
+        u32x4 u;
+        u[0] = bits(x[0]) | (bits(x[1]) << 16);
+        u[1] = bits(x[2]) | (bits(x[3]) << 16);
+        u[2] = bits(x[4]) | (bits(x[5]) << 16);
+        u[3] = bits(x[6]) | (bits(x[7]) << 16);
+        bst16(r, lane * 16, u);
+    }
 };
 
 template <bool NT = false>
@@ -176,8 +239,37 @@ __device__ __forceinline__ void store8f(float *base, int64_t i, const float (&x)
     *reinterpret_cast<f32x4 *>(base + i + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+__device__ __forceinline__ void bload8f(__amdgpu_buffer_rsrc_t r, int32_t lane, float (&x)[kVec]) {
+    const u32x4 a = bld16(r, lane * 32);
+    const u32x4 b = bld16(r, lane * 32 + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[j] = __uint_as_float(a[j]);
+        x[4 + j] = __uint_as_float(b[j]);
+    }
+}
+
+__device__ __forceinline__ void bstore8f(__amdgpu_buffer_rsrc_t r, int32_t lane, const float (&x)[kVec]) {
+    bst16(r, lane * 32, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+    bst16(r, lane * 32 + 16,
+          u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+}
+
 template <>
 struct Elem<DOPT_F32> {
+    static constexpr int64_t kBytes = 4;
+    static __device__ __forceinline__ void bload8(__amdgpu_buffer_rsrc_t r, int32_t lane, float (&x)[kVec]) {
+        bload8f(r, lane, x);
+    }
+    static __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int32_t lane, const float (&x)[kVec]) {
+        bstore8f(r, lane, x);
+    }
+    static __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j) {
+        return bld4(r, lane * 32 + j * 4);
+    }
+    static __device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, int32_t lane, int j, float x) {
+        bst4(r, lane * 32 + j * 4, x);
+    }
     template <bool NT = false>
     static __device__ __forceinline__ Raw8 load_raw(const void *base, int64_t i) {
         const float *f = static_cast<const float *>(base) + i;
@@ -768,12 +860,17 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
         // waited for (arena memory is allocated for every tile); a tile with
         // no param element goes through the per-element path and stores
         // nothing
-        const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
+        const int64_t tile0 = t * kTile;
+        const int32_t lane = threadIdx.x;
+        const auto rg = tile_rsrc(static_cast<const char *>(grad) + tile0 * Elem<GD>::kBytes, kTile * Elem<GD>::kBytes);
+        const auto rp = tile_rsrc(pm + tile0, kTile * 4);
+        const auto rm = tile_rsrc(m + tile0, kTile * 4);
+        const auto rv = tile_rsrc(v + tile0, kTile * 4);
         float g[kVec], p[kVec], a[kVec], b[kVec];
-        Elem<GD>::load8(grad, i0, g);
-        load8f(pm, i0, p);
-        load8f(m, i0, a);
-        load8f(v, i0, b);
+        Elem<GD>::bload8(rg, lane, g);
+        bload8f(rp, lane, p);
+        bload8f(rm, lane, a);
+        bload8f(rv, lane, b);
         TileDesc td{0, kTileFull | (hpre << kTileHgShift)};
         if (!tb.on || ((tb.w[t >> 5] >> (t & 31)) & 1u)) td = tiles[t];
         const int32_t cnt = td.seg_count & kTileCountMask;
@@ -782,21 +879,38 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
             const Hp h = hg == hpre ? h0 : load_hp(rec, hg);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) adamw(g[j], p[j], a[j], b[j], inv, clip_on, clip, h);
-            store8f(pm, i0, p);
-            store8f(m, i0, a);
-            store8f(v, i0, b);
-            if (PD != DOPT_F32) Elem<PD>::store8(param, i0, p);
+            bstore8f(rp, lane, p);
+            bstore8f(rm, lane, a);
+            bstore8f(rv, lane, b);
+            if (PD != DOPT_F32)
+                Elem<PD>::bstore8(tile_rsrc(static_cast<char *>(param) + tile0 * Elem<PD>::kBytes, kTile * Elem<PD>::kBytes),
+                                  lane, p);
         } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                const int64_t e = i0 + j;
-                const int hg = owner_hgroup(segs, td.seg_first, cnt, e);
-                if (hg < 0) continue;
-                adamw(g[j], p[j], a[j], b[j], inv, clip_on, clip, load_hp(rec, hg));
-                pm[e] = p[j];
-                m[e] = a[j];
-                v[e] = b[j];
-                if (PD != DOPT_F32) Elem<PD>::store1(param, e, p[j]);
+            // A boundary tile: walk the segments that meet it (a wave-uniform
+            // loop, so each segment's hyper-group scalars are scalar loads)
+            // and update each of the lane's elements that lies in one.  The
+            // element is read again from the tile (a cache hit) rather than
+            // kept from the loads above, which keeps the kernel's register
+            // count, and so its occupancy, that of the full-tile path.
+            // Segments are disjoint: each element is updated at most once, and
+            // elements of no param are not stored.
+            const int64_t e0 = tile0 + int64_t(lane) * kVec;
+            const auto rq = tile_rsrc(static_cast<char *>(param) + tile0 * Elem<PD>::kBytes, kTile * Elem<PD>::kBytes);
+            for (int32_t sg = td.seg_first; sg < td.seg_first + cnt; ++sg) {
+                const int64_t s0 = segs[sg].start, s1 = segs[sg].end;
+                const Hp hs = load_hp(rec, segs[sg].hgroup);
+#pragma unroll 1
+                for (int j = 0; j < kVec; ++j) {
+                    if (s0 <= e0 + j && e0 + j < s1) {
+                        const int32_t o4 = lane * 32 + j * 4;
+                        float pj = bld4(rp, o4), aj = bld4(rm, o4), bj = bld4(rv, o4);
+                        adamw(Elem<GD>::bload1(rg, lane, j), pj, aj, bj, inv, clip_on, clip, hs);
+                        bst4(rp, o4, pj);
+                        bst4(rm, o4, aj);
+                        bst4(rv, o4, bj);
+                        if (PD != DOPT_F32) Elem<PD>::bstore1(rq, lane, j, pj);
+                    }
+                }
             }
         }
     }
