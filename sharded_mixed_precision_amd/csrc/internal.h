@@ -24,8 +24,12 @@ static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile si
 // the reduction order, and hence the sum of squares, does not depend on the
 // device it runs on.  The large-window grids were chosen by measurement on
 // MI355X: fewer workgroups than the chip could hold keep fewer DRAM rows open
-// at a time, which the read-modify-write and copy passes preferred.
-constexpr int kStatsMaxBlocks = 1024;
+// at a time, which the read-modify-write and copy passes preferred; the
+// read-only pass 1 ran fastest with many more workgroups than the chip holds
+// at once (each then takes few batches), bounded by the cost of adding their
+// partials in the one-workgroup finish.
+constexpr int kStatsMaxBlocks = 16384;
+constexpr int kReduceMaxBlocks = 1024;  // the fused reduce + pass 1
 constexpr int kApplyMaxBlocks = 512;
 constexpr int kCopyMaxBlocks = 256;  // state export / import
 constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which a window counts as small

@@ -160,7 +160,8 @@ static void build_tiles(Buffer &B) {
             if (t < n_tiles) B.stats_tiles[static_cast<size_t>(q * kStatsUnroll + u)] = B.tiles[static_cast<size_t>(t)];
         }
     // the fused reduce + pass 1: one tile per workgroup on small windows
-    B.reduce_grid = n_tiles <= kOneTileGridMax ? static_cast<int32_t>(n_tiles) : B.stats_grid;
+    B.reduce_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
+                                                                    : std::min<int64_t>(n_tiles, kReduceMaxBlocks));
     B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles

@@ -613,32 +613,35 @@ __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict_
     block_sum_store(acc, zeros, out + blockIdx.x);
 }
 
-// One workgroup: the fixed-order sum of all partials into the record, and in
-// the fused form the finalize of the step.  Thread i adds partials i, i+256,
-// ... in order (loads issued together, kFinishBatch at a time), each wave
-// folds its 64 lanes with a fixed butterfly, and thread 0 adds the four wave
-// sums in order.
-constexpr int kFinishBatch = 8;
+// One workgroup of THREADS: the fixed-order sum of all partials into the
+// record, and in the fused form the finalize of the step.  Thread i adds
+// partials i, i+THREADS, ... in order (loads issued together, BATCH at a
+// time), each wave folds its 64 lanes with a fixed butterfly, and thread 0
+// adds the wave sums in order.  Up to kFinishSmall partials (small windows)
+// take 256 threads x 8 loads; more (large windows, up to kStatsMaxBlocks per
+// buffer) take 1024 threads x 16 loads, one round for 16384 partials.
+constexpr int kFinishSmall = 2048;
+constexpr int kFinishBatch = 8;  // loads in flight per thread in k_check_finish
 
-template <bool FINALIZE>
-__global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ part, int32_t n,
-                                                  Record *__restrict__ rec, DevState *__restrict__ st,
-                                                  StepRec *__restrict__ sr, dopt_stats *__restrict__ out,
-                                                  FinalizeArgs fa) {
+template <bool FINALIZE, int THREADS, int BATCH>
+__global__ void __launch_bounds__(THREADS) k_finish(const Partial *__restrict__ part, int32_t n,
+                                                   Record *__restrict__ rec, DevState *__restrict__ st,
+                                                   StepRec *__restrict__ sr, dopt_stats *__restrict__ out,
+                                                   FinalizeArgs fa) {
     const DevState cur = *st;  // loaded now, used after the reduction
     double a = 0.0;
     unsigned long long z = 0;
-    for (int32_t i0 = threadIdx.x; i0 < n; i0 += kFinishBatch * kBlock) {
-        Partial q[kFinishBatch];
+    for (int32_t i0 = threadIdx.x; i0 < n; i0 += BATCH * THREADS) {
+        Partial q[BATCH];
 #pragma unroll
-        for (int j = 0; j < kFinishBatch; ++j) {
-            const int32_t i = i0 + j * kBlock;
+        for (int j = 0; j < BATCH; ++j) {
+            const int32_t i = i0 + j * THREADS;
             q[j] = part[i < n ? i : n - 1];
         }
         __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first add
 #pragma unroll
-        for (int j = 0; j < kFinishBatch; ++j) {
-            const bool in = i0 + j * kBlock < n;  // a clamped duplicate adds +0
+        for (int j = 0; j < BATCH; ++j) {
+            const bool in = i0 + j * THREADS < n;  // a clamped duplicate adds +0
             a += in ? q[j].sumsq : 0.0;
             z += in ? q[j].zeros : 0ull;
         }
@@ -648,8 +651,8 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
         a += __shfl_xor(a, off, 64);
         z += __shfl_xor(z, off, 64);
     }
-    __shared__ double s_acc[kBlock / 64];
-    __shared__ unsigned long long s_z[kBlock / 64];
+    __shared__ double s_acc[THREADS / 64];
+    __shared__ unsigned long long s_z[THREADS / 64];
     __shared__ double s_tot[2];
     if ((threadIdx.x & 63) == 0) {
         s_acc[threadIdx.x >> 6] = a;
@@ -660,7 +663,7 @@ __global__ void __launch_bounds__(kBlock) k_finish(const Partial *__restrict__ p
         double t = 0.0;
         unsigned long long tz = 0;
 #pragma unroll
-        for (int w = 0; w < kBlock / 64; ++w) {
+        for (int w = 0; w < THREADS / 64; ++w) {
             t += s_acc[w];
             tz += s_z[w];
         }
@@ -1091,11 +1094,15 @@ static int build_finalize_args(const dopt_layout *L, const dopt_hparams *hp, int
 // FINALIZE is set.
 template <bool FINALIZE>
 static int launch_finish(int32_t n_partials, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
-    k_finish<FINALIZE><<<1, kBlock, 0, stream>>>(reinterpret_cast<const Partial *>(ws_ptr(ws, kWsPartials)),
-                                                 n_partials, reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord)),
-                                                 reinterpret_cast<DevState *>(ws_ptr(ws, kWsState)),
-                                                 reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec)),
-                                                 reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats)), fa);
+    const Partial *part = reinterpret_cast<const Partial *>(ws_ptr(ws, kWsPartials));
+    Record *rec = reinterpret_cast<Record *>(ws_ptr(ws, kWsRecord));
+    DevState *st = reinterpret_cast<DevState *>(ws_ptr(ws, kWsState));
+    StepRec *sr = reinterpret_cast<StepRec *>(ws_ptr(ws, kWsStepRec));
+    dopt_stats *out = reinterpret_cast<dopt_stats *>(ws_ptr(ws, kWsStats));
+    if (n_partials <= kFinishSmall)
+        k_finish<FINALIZE, 256, 8><<<1, 256, 0, stream>>>(part, n_partials, rec, st, sr, out, fa);
+    else
+        k_finish<FINALIZE, 1024, 16><<<1, 1024, 0, stream>>>(part, n_partials, rec, st, sr, out, fa);
     return check_launch("launch k_finish");
 }
 
