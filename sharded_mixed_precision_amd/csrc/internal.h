@@ -70,7 +70,7 @@ struct TileBits {
 // elements, so an 8-element vector is either wholly inside a bucket or past
 // its end); one partial per check tile.
 constexpr int64_t kCheckTile = 8 * kTile;
-constexpr int kCheckMaxBlocks = 2048;
+constexpr int kCheckMaxBlocks = 4096;
 struct CheckBucket {
     int64_t offset, numel, tile_base;  // tile_base: index of the bucket's first check tile
 };
