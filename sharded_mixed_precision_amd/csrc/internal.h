@@ -30,7 +30,7 @@ static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile si
 // partials in the one-workgroup finish.
 constexpr int kStatsMaxBlocks = 16384;
 constexpr int kReduceMaxBlocks = 1024;  // the fused reduce + pass 1
-constexpr int kApplyMaxBlocks = 512;
+constexpr int kApplyMaxBlocks = 256;
 constexpr int kCopyMaxBlocks = 256;  // state export / import
 constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which a window counts as small
 // Grad windows above this size are streamed through pass 1 with
