@@ -42,9 +42,9 @@ APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    "gpt2-small": {"src": "75da29bf8f5e629c", "bytes_per_launch": 437048474},
+    "gpt2-small": {"src": "579f2890d6dfe5ef", "bytes_per_launch": 436654592},
     # both buffers' pass-2 launches of one step (bf16 params with fp32 grads + fp32 norms)
-    "llama3-8b": {"src": "75da29bf8f5e629c", "bytes_per_launch": 30219914281},
+    "llama3-8b": {"src": "579f2890d6dfe5ef", "bytes_per_launch": 30176799519},
 }
 
 
