@@ -122,6 +122,30 @@ def test_split_api_matches_one_call():
     H.run_full(H.Case("split", params, 4, 2, steps=4), split_steps=(1, 3), half_steps=(2,))
 
 
+def test_split_api_large_window():
+    """A window of more than 8192 tiles: pass 1 runs on its large-window grid
+    (more than 2048 partials), so the reduction of the split API (no
+    finalize) and of the fused step both take the 1024-thread finish."""
+    import sharded_mixed_precision_amd as D
+    params = [ParamSpec("a", 25_000_003, "bf16", "bf16"), ParamSpec("b", 24_999_999, "bf16", "bf16"),
+              ParamSpec("n", 4096, "f32", "f32")]
+    L = D.dopt_build_ranges(params, 2, 1)
+    b0 = L.buffer(0)
+    assert b0["arena_numel"] // D.DOPT_ARENA_ALIGN > 8192
+    H.run_full(H.Case("split-large", params, 2, 1, steps=3), split_steps=(1, 3), half_steps=(2,))
+
+
+def test_many_tiny_params():
+    """About 3000 params of 1 to 100 elements (64-element aligned starts): nearly
+    every tile is a boundary tile holding up to 32 shards, the worst case of
+    the per-element ownership walk in both passes; three hyper-groups."""
+    rng = np.random.default_rng(7)
+    sizes = rng.integers(1, 101, size=3000)
+    params = [ParamSpec(f"t{i}", int(n), "bf16", "bf16", 0, i % 3) for i, n in enumerate(sizes)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
+    H.run_full(H.Case("tiny-params", params, 3, 1, bucket_size=40_000, steps=3, hparams=hps))
+
+
 def test_deterministic():
     case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
     case.steps = 2
