@@ -77,6 +77,33 @@ def test_first_step_closed_form():
     assert np.array_equal(run.bufs[0]["param"], to_bits(torch.from_numpy(run.bufs[0]["master"]).to(torch.bfloat16)))
 
 
+def test_decay_multiplies_the_weight_before_the_adam_term():
+    """Decoupled weight decay scales the pre-step weight: p1 = p0 (1 - lr wd)
+    - lr g / (|g| + eps).  With lr = 0.1 and wd = 0.5 the other placement,
+    (p0 - lr g / (|g| + eps)) (1 - lr wd), differs by lr^2 wd ~ 5e-3 per
+    element, far above rounding."""
+    n = 2048
+    lr, wd = 0.1, 0.5
+    run = _single(n, "f32", "f32")
+    rng = np.random.default_rng(3)
+    run.bufs[0]["param"][:] = rng.standard_normal(n).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    g[g == 0] = 1e-3
+    _set_grads(run, 0, g)
+    run.init_state()
+    p0 = run.bufs[0]["param"].astype(np.float64).copy()
+    run.step([(lr, B1, B2, EPS, wd)], 0.0)
+    p1 = run.bufs[0]["param"].astype(np.float64)
+    gd = g.astype(np.float64)
+    u = gd / (np.abs(gd) + EPS)
+    want = p0 * (1 - lr * wd) - lr * u
+    other = (p0 - lr * u) * (1 - lr * wd)
+    # fp32 rounding of each term (the weight, the decayed weight, the Adam term)
+    tol = 4 * (_ulp(p0) + _ulp(lr * u) + _ulp(p1))
+    assert np.all(np.abs(p1 - want) <= tol)
+    assert np.all(np.abs(p1 - other) > 100 * tol)
+
+
 def test_constant_gradient_geometric_series():
     n, T = 512, 25
     run = _single(n, "f32", "f32")
