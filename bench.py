@@ -35,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "shard AdamW step: Gparams/s and achieved HBM GB/s (% of peak), 1 MI355X"
 ES = {"f32": 4, "bf16": 2, "f16": 2}
 APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
+SMALL_WINDOW = 64 << 20  # shard elements up to which the default step counts are large
 
 # HBM traffic of k_apply measured with rocprofv3 PMC counters (FETCH_SIZE,
 # WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
@@ -292,8 +293,10 @@ def bench_checkpoint(args, w, L, A, bufs_c, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 500 on windows of up to 64M shard elements, else 10)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 200 on windows of up to 64M shard elements, else 3)")
     ap.add_argument("--workload", default="gpt2-small")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -354,6 +357,15 @@ def main():
                                                    w.weight_sigma))
         A.bufs[k]["grad"].copy_(synth.fill_normal(info["gd"], info["n"], w.seed, synth.grad_stream(k), 1,
                                                   w.grad_sigma, scale=w.initial_scale, zero_frac=w.zero_frac))
+    # A small window's step lasts tens of microseconds: hundreds of warm-up
+    # steps let the clocks settle, and hundreds of timed steps keep the timed
+    # region in the tens of milliseconds.  A large window's step lasts
+    # milliseconds.
+    small = E <= SMALL_WINDOW
+    if args.steps is None:
+        args.steps = 500 if small else 10
+    if args.warmup is None:
+        args.warmup = 200 if small else 3
     D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
     bufs_c = D.tensors(A.bufs)
     hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
