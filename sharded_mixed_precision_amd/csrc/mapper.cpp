@@ -162,7 +162,7 @@ static void build_tiles(Buffer &B) {
     // the fused reduce + pass 1: one tile per workgroup on small windows
     B.reduce_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                     : std::min<int64_t>(n_tiles, kReduceMaxBlocks));
-    B.apply_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
+    B.apply_grid = static_cast<int32_t>(n_tiles <= kApplyOneTileMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                   : std::min<int64_t>(n_tiles, kCopyMaxBlocks));
