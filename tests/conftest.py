@@ -11,6 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD GPU (MI355X / gfx950) and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU test")
+    config.addinivalue_line("markers", "gpu_fullsize: every element of a full-size workload against the oracle "
+                                       "(minutes; run on request with -m gpu_fullsize, not part of -m gpu)")
 
 
 @pytest.fixture(scope="session", autouse=True)

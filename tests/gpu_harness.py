@@ -303,6 +303,7 @@ def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[i
             # slots that hold no param element are never written
             assert np.array_equal(pdev[~m], init_bits[k][~m]), f"step {s}: param arena gap written"
         report.append(rep)
+        log(f"[parity] {case.name} step {s}: every element compared ({time.time() - t0:.1f}s)")
     log(f"[parity] {case.name}: {case.steps} steps full compare ok in {time.time() - t0:.1f}s; last {report[-1]}")
     return report
 
