@@ -139,14 +139,16 @@ def ulp_dist(a_bits: np.ndarray, b_bits: np.ndarray, dt: str) -> np.ndarray:
 def check_f32(name: str, dev: np.ndarray, ref: np.ndarray) -> dict:
     dev = dev.astype(np.float64)
     ref = ref.astype(np.float64)
-    err = np.abs(dev - ref)
+    with np.errstate(invalid="ignore"):  # inf - inf where both overflowed
+        err = np.abs(dev - ref)
     tol = np.maximum(MASTER_RTOL * np.abs(ref), MASTER_ATOL)
-    bad = ~(err <= tol)
+    bad = ~((err <= tol) | (dev == ref))  # equal infinities (an overflowed v) match
     if bad.any():
         i = np.flatnonzero(bad)[:5]
         raise AssertionError(f"{name}: {bad.sum()} of {bad.size} outside tolerance; idx {i} dev {dev[i]} ref {ref[i]}")
+    rel = np.where(dev == ref, 0.0, err / np.maximum(np.abs(ref), 1e-30))
     return {"n": int(dev.size), "bit_exact": float(np.mean(dev == ref)) if dev.size else 1.0,
-            "max_rel": float(np.max(err / np.maximum(np.abs(ref), 1e-30))) if dev.size else 0.0}
+            "max_rel": float(np.max(rel)) if dev.size else 0.0}
 
 
 def check_param(name: str, dev_bits: np.ndarray, ref_bits: np.ndarray, dt: str) -> dict:

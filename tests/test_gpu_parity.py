@@ -146,6 +146,19 @@ def test_many_tiny_params():
     H.run_full(H.Case("tiny-params", params, 3, 1, bucket_size=40_000, steps=3, hparams=hps))
 
 
+def test_extreme_magnitudes():
+    """Grads at both ends of the fp32 range, fp32 and bf16 grad buffers.
+    Subnormal grads (sigma 1e-38) must be kept, not flushed to zero, in both
+    passes.  Grads near 1e37 are finite, their double sum of squares too, but
+    g*g overflows fp32 in the moment update when nothing clips them, so v and
+    its square root become +inf and the Adam term 0; with clipping the grads
+    are scaled to tiny values first."""
+    params = [ParamSpec("a", 20_000, "bf16", "f32"), ParamSpec("b", 3_000, "bf16", "bf16")]
+    H.run_full(H.Case("subnormal", params, 2, 1, steps=3, grad_sigma=1e-38))
+    H.run_full(H.Case("huge-noclip", params, 2, 1, steps=2, grad_sigma=1e37, max_norm=0.0))
+    H.run_full(H.Case("huge-clip", params, 2, 1, steps=2, grad_sigma=1e37))
+
+
 def test_deterministic():
     case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
     case.steps = 2
