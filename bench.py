@@ -43,9 +43,9 @@ SMALL_WINDOW = 64 << 20  # shard elements up to which the default step counts ar
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    "gpt2-small": {"src": "d1ad01f3f879772d", "bytes_per_launch": 436862475},
+    "gpt2-small": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 436782049},
     # both buffers' pass-2 launches of one step (bf16 params with fp32 grads + fp32 norms)
-    "llama3-8b": {"src": "d1ad01f3f879772d", "bytes_per_launch": 30176766044},
+    "llama3-8b": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 30176653619},
 }
 
 
@@ -305,6 +305,9 @@ def main():
                          "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare); check: the whole-bucket "
                          "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads); checkpoint: the "
                          "model-space export and import of the rank's optimizer state (dopt_state_export / _import)")
+    ap.add_argument("--placement-tries", type=int, default=8,
+                    help="candidate arena placements tried at start-up, the fastest for pass 2 kept (1: plain "
+                         "allocation); capped by free device memory")
     ap.add_argument("--flush-llc", action="store_true",
                     help="step mode: write a 512 MiB buffer before each timed step, so that no step data is left in "
                          "the 256 MB last-level cache; each step is then timed on its own with HIP events and "
@@ -343,7 +346,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     params = synth.PARAM_LISTS[w.model]()
     L = D.dopt_build_ranges(params, w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
-    A = DeviceArenas(L)
+    A = DeviceArenas(L, placement_tries=args.placement_tries)
     stream = torch.cuda.current_stream()
     E = 0
     bytes_step = 0
@@ -460,7 +463,8 @@ def main():
         "config": {"workload": f"{w.name}: {len(params)}-param list, rank {w.dp_rank} of N={w.dp_size}, "
                                f"bucket {w.bucket_size}, {E} shard elements",
                    "shard_elements": E, "bytes_per_step": bytes_step,
-                   "llc": "flushed before each step" if args.flush_llc else "warm (steps back to back)"},
+                   "llc": "flushed before each step" if args.flush_llc else "warm (steps back to back)",
+                   "arena_placement": A.placement or {"candidates": 1}},
         "hbm_GBps_step": round(gbps, 1),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),

@@ -29,6 +29,11 @@ static_assert(kTile == DOPT_ARENA_ALIGN, "arena alignment must equal the tile si
 // at once (each then takes few batches), bounded by the cost of adding their
 // partials in the one-workgroup finish.
 constexpr int kStatsMaxBlocks = 16384;
+// fp32 grads keep 8 16-byte loads in flight per lane (two per tile), which
+// one workgroup per CU turns into the full read rate (Llama-3-8B rank: pass 1
+// + finish 0.56-0.57 ms at 256 workgroups, 0.60 ms at 16384); 16-bit grads,
+// with 4 loads in flight, need the many-workgroup grid above.
+constexpr int kStatsMaxBlocksF32 = 256;
 constexpr int kReduceMaxBlocks = 1024;  // the fused reduce + pass 1
 constexpr int kApplyMaxBlocks = 256;
 constexpr int kCopyMaxBlocks = 256;  // state export / import

@@ -137,8 +137,9 @@ static void build_tiles(Buffer &B) {
         B.tiles[t] = TileDesc{static_cast<int32_t>(s), cnt | flags};
     }
     const int64_t stats_one_pass = (n_tiles + kStatsUnroll - 1) / kStatsUnroll;
+    const int64_t stats_max = B.gd == DOPT_F32 ? kStatsMaxBlocksF32 : kStatsMaxBlocks;
     B.stats_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? stats_one_pass
-                                                                   : std::min<int64_t>(stats_one_pass, kStatsMaxBlocks));
+                                                                   : std::min<int64_t>(stats_one_pass, stats_max));
     // pass 2's boundary bitmap (see TileBits)
     B.bits.on = 0;
     B.bits.hg = 0;

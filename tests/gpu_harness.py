@@ -65,6 +65,7 @@ class Case:
     wire: str = "bf16"
     reduce_scale: float = 1.0
     reduce_split: bool = False
+    placement_tries: int = 1  # DeviceArenas placement search (1: plain allocation)
 
     def scale_at(self, step: int) -> float:
         if not self.dynamic:
@@ -190,7 +191,7 @@ class DeviceRun:
         self.D = D
         self.L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw,
                                      case.instances)
-        self.A = DeviceArenas(self.L)
+        self.A = DeviceArenas(self.L, placement_tries=case.placement_tries)
         self.stream = torch.cuda.current_stream()
         self.case = case
 

@@ -159,6 +159,17 @@ def test_extreme_magnitudes():
     H.run_full(H.Case("huge-clip", params, 2, 1, steps=2, grad_sigma=1e37))
 
 
+def test_placement_search_arenas():
+    """Arenas chosen by the placement search (the kept candidate zeroed, the
+    others freed) carry the step exactly like a plain allocation."""
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.name, case.steps, case.placement_tries = "gpt2-placement", 3, 3
+    dev = H.DeviceRun(case)
+    assert dev.A.placement["candidates"] == 3 and len(dev.A.placement["pass2_ms"]) == 3
+    del dev
+    H.run_full(case)
+
+
 def test_deterministic():
     case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
     case.steps = 2
