@@ -27,6 +27,10 @@ int fail(int code, const std::string &msg) {
 
 static int64_t align_up(int64_t x, int64_t d) { return (x + d - 1) / d * d; }
 
+// The largest element count a param list may hold (far above any device
+// memory): every padded offset then stays far from the int64 limit.
+static constexpr int64_t kMaxListNumel = int64_t(1) << 52;
+
 static bool valid_dtype(int32_t d) { return d == DOPT_F32 || d == DOPT_BF16 || d == DOPT_F16; }
 
 // Lay one flat buffer out in buckets ([DO] "Bucket 划分算法：逆序遍历 + 尺寸触发",
@@ -175,12 +179,18 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
     L.num_instances = cfg->num_instances > 0 ? cfg->num_instances : 1;
     L.N = L.dp_size / L.num_instances;  // ranks of one distributed-optimizer instance
     L.r = L.dp_rank % L.N;              // this rank inside its instance
+    // param indices are kept in 32 bits in the segment table
+    if (n > INT32_MAX) return fail(DOPT_ERR_INVALID, "more than INT32_MAX params");
     L.params.resize(static_cast<size_t>(n));
+    int64_t total = 0;
     for (int64_t i = 0; i < n; ++i) {
         const dopt_param_desc &d = params[i];
-        if (d.numel <= 0 || !valid_dtype(d.param_dtype) || !valid_dtype(d.grad_dtype) || d.hgroup < 0 ||
-            d.hgroup >= DOPT_MAX_HGROUPS)
+        if (d.numel <= 0 || d.numel > kMaxListNumel || !valid_dtype(d.param_dtype) || !valid_dtype(d.grad_dtype) ||
+            d.hgroup < 0 || d.hgroup >= DOPT_MAX_HGROUPS)
             return fail(DOPT_ERR_INVALID, "param " + std::to_string(i) + ": bad numel, dtype or hgroup");
+        total += d.numel;
+        if (total > kMaxListNumel)
+            return fail(DOPT_ERR_INVALID, "the params hold more than 2^52 elements in total");
         Param &p = L.params[i];
         p.numel = d.numel;
         p.pd = d.param_dtype;

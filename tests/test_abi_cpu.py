@@ -105,6 +105,12 @@ def test_mapper_errors():
         d.dopt_build_ranges([ParamSpec("z", 0, "bf16", "bf16")], 1, 0)
     with pytest.raises(d.DoptError):
         d.dopt_build_ranges([ParamSpec("z", 5, "bf16", "bf16", 0, 16)], 1, 0)
+    # element counts that would overflow the padded 64-bit offsets
+    for big in ([ParamSpec("h", 1 << 62, "bf16", "bf16")],
+                [ParamSpec("h", 3 << 50, "bf16", "bf16"), ParamSpec("i", 3 << 50, "f32", "f32")]):
+        with pytest.raises(d.DoptError) as e:
+            d.dopt_build_ranges(big, 8, 0)
+        assert e.value.code == -1
     L = d.dopt_build_ranges(ok, 2, 1)
     with pytest.raises(d.DoptError) as e:
         L.buffer(3)
