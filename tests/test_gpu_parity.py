@@ -75,6 +75,22 @@ def test_mixed_dtypes_hgroups_lone_buckets():
     H.run_full(H.Case("mixed", params, 3, 1, bucket_size=5000, steps=4, hparams=hps))
 
 
+def test_every_dtype_pair():
+    """All nine (param dtype, grad dtype) pairs, one flat buffer each of two
+    params in two buckets, with window ends that cut params and
+    tiles."""
+    dts = ["f32", "bf16", "f16"]
+    pairs = [(pd, gd) for pd in dts for gd in dts]
+    params = []
+    for i, (pd, gd) in enumerate(pairs):
+        params += [ParamSpec(f"{pd}-{gd}-a", 9_001 + 2_048 * i, pd, gd, 0, i % 3),
+                   ParamSpec(f"{pd}-{gd}-b", 3_001 + 517 * i, pd, gd, 0, (i + 1) % 3)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
+    for r in (0, 2):
+        rep = H.run_full(H.Case(f"dtype-pairs-r{r}", params, 3, r, bucket_size=2_500, steps=3, hparams=hps))
+        assert sum(1 for k in rep[-1] if k.startswith("param")) == 9
+
+
 def test_one_nonzero_hgroup_full_tiles():
     """Every shard of the buffer in hyper-group 2, with tiles wholly inside one
     shard: pass 2 takes such tiles' AdamW scalars from the group it loaded
