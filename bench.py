@@ -67,8 +67,35 @@ def pass_bytes(pd: str, gd: str):
     return p1, p2
 
 
+def host_cpu() -> dict:
+    """The host's processor model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(workload, seconds: float):
-    """The oracle (plain single-threaded C) on a bounded sample of the same workload."""
+    """The oracle (plain single-threaded C) on a bounded sample of the same
+    workload, with the calling thread pinned to one core for the timing."""
+    mask = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(mask)})
+    try:
+        res = _cpu_baseline(workload, seconds)
+    finally:
+        os.sched_setaffinity(0, mask)
+    res["host"] = host_cpu()
+    res["host"]["pinned_core"] = min(mask)
+    return res
+
+
+def _cpu_baseline(workload, seconds: float):
     import numpy as np
     import oracle
     import synth

@@ -31,3 +31,8 @@ def test_traffic_is_reported_only_for_the_measured_source():
     for entry in bench.MEASURED_TRAFFIC.values():
         assert len(entry["src"]) == 16 and entry["bytes_per_launch"] > 0
     assert len(bench._src_sha()) == 16
+
+
+def test_cpu_baseline_host_description():
+    h = bench.host_cpu()
+    assert h["cores_available"] >= 1 and isinstance(h["model"], str) and h["model"]
