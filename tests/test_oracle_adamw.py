@@ -336,3 +336,57 @@ def test_hyper_groups_use_their_own_lr():
         a = p["arena_offset"]
         upd = 0.5 - run.bufs[0]["param"][a:a + 640].astype(np.float64)
         assert np.allclose(upd, lr, rtol=1e-5)
+
+
+@pytest.mark.parametrize("max_norm", [0.0, 0.05])
+def test_steps_track_fp64_adamw(max_norm):
+    """Six steps of the oracle on generic inputs (fresh normal grads each
+    step, two hyper-groups, weight decay, clipping off or active on every
+    step) against the textbook AdamW recurrences evaluated in fp64 from the
+    same fp32 start and the same fp32 grads: m, v, m_hat = m / (1 - b1^t),
+    v_hat = v / (1 - b2^t), p <- p (1 - lr wd) - lr m_hat / (sqrt(v_hat) + eps),
+    after clipping g by max_norm / (norm + 1e-6) when that is below 1.  The
+    fp32 oracle may differ only by its roundings: a few ulps of p per step,
+    and 1e-6 of the size of the terms in m and v."""
+    params = [ParamSpec("a", 3000, "bf16", "bf16", 0, 0), ParamSpec("b", 1500, "bf16", "bf16", 0, 1)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-3, 0.8, 0.99, 1e-6, 0.1)]
+    run = OracleRun(params, 1, 0, 0)
+    _set_params_normal(run, 0)
+    run.init_state()
+    b = run.bufs[0]
+    ok = run.valid(0)
+    hg = np.zeros(b["n"], np.int64)
+    for i in range(2):
+        p = run.L.param(i)
+        hg[p["arena_offset"]:p["arena_offset"] + (p["param"][1] - p["param"][0])] = i
+    lr, b1, b2, eps, wd = (np.array([h[j] for h in hps])[hg] for j in range(5))
+    p64 = b["master"].astype(np.float64)
+    m64 = np.zeros(b["n"])
+    v64 = np.zeros(b["n"])
+    sm = np.zeros(b["n"])  # running size of the terms summed into m
+    for t in range(1, 7):
+        x = synth.normal_f32(0, synth.STREAM_GRAD, t, 0, b["n"], 1e-3)
+        t16 = torch.from_numpy(x).to(torch.bfloat16)
+        b["grad"][:] = to_bits(t16)
+        g = t16.float().numpy().astype(np.float64)
+        g[~ok] = 0.0
+        norm = math.sqrt(float(np.sum(g * g)))
+        if max_norm > 0 and max_norm / (norm + 1e-6) < 1.0:
+            g = g * (max_norm / (norm + 1e-6))
+        stats = run.step(hps, max_norm)
+        assert stats.found_inf == 0
+        assert abs(stats.norm - norm) <= 1e-12 * norm
+        p64 = p64 * (1.0 - lr * wd)
+        m64 = b1 * m64 + (1.0 - b1) * g
+        v64 = b2 * v64 + (1.0 - b2) * g * g
+        sm = b1 * sm + (1.0 - b1) * np.abs(g)
+        mhat = m64 / (1.0 - b1 ** t)
+        vhat = v64 / (1.0 - b2 ** t)
+        p64 = p64 - lr * mhat / (np.sqrt(vhat) + eps)
+        dm = np.abs(b["m"].astype(np.float64) - m64)[ok]
+        dv = np.abs(b["v"].astype(np.float64) - v64)[ok]
+        dp = np.abs(b["master"].astype(np.float64) - p64)[ok]
+        assert np.all(dm <= 1e-6 * sm[ok]), f"step {t}: m off by {np.max(dm / sm[ok]):.3g} of its terms"
+        assert np.all(dv <= 1e-6 * v64[ok]), f"step {t}: v off by {np.max(dv / v64[ok]):.3g}"
+        tol_p = t * (4 * _ulp(p64[ok]) + lr[ok] * 1e-5)
+        assert np.all(dp <= tol_p), f"step {t}: master off by {np.max(dp / tol_p):.3g} of the bound"
