@@ -13,13 +13,13 @@ With ``placement_tries = n > 1`` the allocator creates up to n candidate sets
 of arenas, each while the earlier ones are still held (so each gets other
 pages), times the second pass on each (zeroed data, through the C ABI), keeps
 the fastest and frees the rest.  The number of whole sets is capped by the
-free device memory; when fewer than four fit (a rank holding about a third of
-the card or more), the kept set is then refined one array at a time: up to
-n candidates for that array, the others fixed, the fastest kept.  (Refining
-array by array did not find the fast placements of the 16 GB Llama-3 ranks,
-which whole sets did, but moved the 108 GB dense-7B state from 34.4 to
-31.2 ms.)  The search runs once, before any data is loaded; the arenas then
-serve every step of the run.
+free device memory.  The kept set is then refined one array at a time: up to
+n candidates for that array, the others fixed, the fastest kept.  (Whole sets
+found the fast placements of the 16 GB Llama-3 ranks, which refining array by
+array alone did not; refining the best whole set took their step a further
+0.5-1% faster, and the 108 GB dense-7B state, of which only two sets fit,
+from 34.4 to 31.2 ms.)  The search runs once, before any data is loaded; the
+arenas then serve every step of the run.
 """
 from __future__ import annotations
 
@@ -108,13 +108,12 @@ class DeviceArenas:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         self.placement = {"candidates": len(times), "pass2_ms": [round(x, 4) for x in times], "kept": best}
-        if len(times) < 4:
-            self.placement["refined"] = self._refine(kept, tries, launches)
-            for t in kept[0]:
-                for v in t.values():
-                    if v is not None:
-                        v.zero_()
-            kept[1].zero_()
+        self.placement["refined"] = self._refine(kept, tries, launches)
+        for t in kept[0]:
+            for v in t.values():
+                if v is not None:
+                    v.zero_()
+        kept[1].zero_()
         return kept
 
     def _refine(self, kept, tries: int, launches: int) -> List:

@@ -176,12 +176,14 @@ def test_extreme_magnitudes():
 
 
 def test_placement_search_arenas():
-    """Arenas chosen by the placement search (the kept candidate zeroed, the
-    others freed) carry the step exactly like a plain allocation."""
+    """Arenas chosen by the placement search (the kept candidate set refined
+    array by array and zeroed, the others freed) carry the step exactly like a
+    plain allocation."""
     case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
     case.name, case.steps, case.placement_tries = "gpt2-placement", 3, 3
     dev = H.DeviceRun(case)
     assert dev.A.placement["candidates"] == 3 and len(dev.A.placement["pass2_ms"]) == 3
+    assert [r[1] for r in dev.A.placement["refined"]] == ["grad", "param", "master", "exp_avg", "exp_avg_sq"]
     del dev
     H.run_full(case)
 
