@@ -373,7 +373,10 @@ def main():
     w = synth.WORKLOADS[args.workload]
     params = synth.PARAM_LISTS[w.model]()
     L = D.dopt_build_ranges(params, w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
+    t_alloc = time.perf_counter()
     A = DeviceArenas(L, placement_tries=args.placement_tries)
+    torch.cuda.synchronize()
+    t_alloc = time.perf_counter() - t_alloc
     stream = torch.cuda.current_stream()
     E = 0
     bytes_step = 0
@@ -491,7 +494,7 @@ def main():
                                f"bucket {w.bucket_size}, {E} shard elements",
                    "shard_elements": E, "bytes_per_step": bytes_step,
                    "llc": "flushed before each step" if args.flush_llc else "warm (steps back to back)",
-                   "arena_placement": A.placement or {"candidates": 1}},
+                   "arena_placement": {**(A.placement or {"candidates": 1}), "seconds": round(t_alloc, 3)}},
         "hbm_GBps_step": round(gbps, 1),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),
