@@ -413,13 +413,12 @@ void or_f16_to_f32_n(const uint16_t *x, float *y, int64_t n) {
 }
 
 /* A table of the 65536 binary16 values, filled from or_f16_to_f32, so that
- * large stats passes do not decode every element again. */
+ * large stats passes do not decode every element again.  It is filled once,
+ * when the library is loaded (before any caller thread can run), and only
+ * read afterwards, so callers on several threads share it without a race. */
 static float g_f16_table[65536];
-static int g_f16_table_ready = 0;
-static void f16_table_init(void) {
-    if (g_f16_table_ready) return;
+__attribute__((constructor)) static void f16_table_init(void) {
     for (uint32_t h = 0; h < 65536u; ++h) g_f16_table[h] = or_f16_to_f32((uint16_t)h);
-    g_f16_table_ready = 1;
 }
 
 static float load_f32(const void *base, int32_t dt, int64_t i) {
@@ -450,7 +449,6 @@ static void store_param(void *base, int32_t dt, int64_t i, float x) {
  */
 void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t wire_dtype, int32_t n_chunks,
                       int64_t stride, float scale, int64_t lo, int64_t hi, void *grad_out) {
-    f16_table_init();
     const ob_buffer *B = &L->buf[k];
     if (hi > B->window_numel) hi = B->window_numel;
     for (int64_t i = lo; i < hi; ++i) {
@@ -477,7 +475,6 @@ void or_reduce_chunks(const or_layout *L, int32_t k, const void *chunks, int32_t
  */
 void or_check_bucket(const or_layout *L, int32_t k, int32_t b, const void *grad, int64_t lo, int64_t hi, double thr,
                      double *out_sumsq, float *out_max, int32_t *out_flags) {
-    f16_table_init();
     const ob_buffer *B = &L->buf[k];
     const ob_bucket *bk = &B->buckets[b];
     if (lo < bk->offset) lo = bk->offset;
@@ -514,7 +511,6 @@ void or_check_bucket(const or_layout *L, int32_t k, int32_t b, const void *grad,
  * separate master ([ZL] §3).
  */
 void or_init_state(const or_layout *L, or_arrays *bufs) {
-    f16_table_init();
     for (int32_t k = 0; k < L->n_buffers; ++k) {
         const ob_buffer *B = &L->buf[k];
         for (int64_t s = 0; s < B->n_segs; ++s) {
@@ -545,7 +541,6 @@ float or_inv_scale(const or_scaler *sc) { return (float)(1.0 / sc->scale); }
  */
 void or_grad_stats_range(const or_layout *L, int32_t k, const void *grad, float inv_scale, int64_t lo, int64_t hi,
                          or_stats *st) {
-    f16_table_init();
     double sumsq = 0.0;
     uint64_t zeros = 0;
     int32_t found_inf = 0;
@@ -568,7 +563,6 @@ void or_grad_stats_range(const or_layout *L, int32_t k, const void *grad, float 
 }
 
 void or_grad_stats(const or_layout *L, const or_arrays *bufs, float inv_scale, or_stats *st) {
-    f16_table_init();
     double sumsq = 0.0;
     uint64_t zeros = 0;
     int32_t found_inf = 0;
@@ -689,7 +683,6 @@ static inline void adamw_elem(float raw, float *p, float *m, float *v, const or_
 
 void or_apply(const or_layout *L, or_arrays *bufs, const or_scalars *s) {
     if (s->skip) return;
-    f16_table_init();
     for (int32_t k = 0; k < L->n_buffers; ++k) {
         const ob_buffer *B = &L->buf[k];
         for (int64_t q = 0; q < B->n_segs; ++q) {
@@ -712,7 +705,6 @@ void or_apply(const or_layout *L, or_arrays *bufs, const or_scalars *s) {
 void or_apply_elems(int32_t param_dtype, int32_t grad_dtype, int64_t n, const int32_t *hgroup, const void *grad,
                     float *master, float *m, float *v, void *param_out, const or_scalars *s) {
     if (s->skip) return;
-    f16_table_init();
     for (int64_t i = 0; i < n; ++i) {
         float raw = load_f32(grad, grad_dtype, i);
         adamw_elem(raw, &master[i], &m[i], &v[i], s, hgroup ? hgroup[i] : 0);

@@ -40,18 +40,21 @@ def gpt2_small(dt: str = "bf16", gdt: str = "bf16") -> List[ParamSpec]:
 
 def _llama(L: int, h: int, nq: int, nkv: int, hd: int, ffn: int, vocab: int, mat_dt: str, mat_gdt: str,
            norm_dt: str, norm_gdt: str) -> List[ParamSpec]:
+    # Forward order inside a layer: input norm, attention, post-attention
+    # norm, MLP (the order the layer runs them, which is the order a
+    # Megatron-style layer registers them; its buckets fill in reverse).
     ps = [ParamSpec("embed_tokens", vocab * h, mat_dt, mat_gdt)]
     for i in range(L):
         p = f"layers.{i}."
-        ps += [ParamSpec(p + "q_proj", h * nq * hd, mat_dt, mat_gdt),
+        ps += [ParamSpec(p + "input_layernorm", h, norm_dt, norm_gdt),
+               ParamSpec(p + "q_proj", h * nq * hd, mat_dt, mat_gdt),
                ParamSpec(p + "k_proj", h * nkv * hd, mat_dt, mat_gdt),
                ParamSpec(p + "v_proj", h * nkv * hd, mat_dt, mat_gdt),
                ParamSpec(p + "o_proj", nq * hd * h, mat_dt, mat_gdt),
+               ParamSpec(p + "post_attention_layernorm", h, norm_dt, norm_gdt),
                ParamSpec(p + "gate_proj", h * ffn, mat_dt, mat_gdt),
                ParamSpec(p + "up_proj", h * ffn, mat_dt, mat_gdt),
-               ParamSpec(p + "down_proj", ffn * h, mat_dt, mat_gdt),
-               ParamSpec(p + "input_layernorm", h, norm_dt, norm_gdt),
-               ParamSpec(p + "post_attention_layernorm", h, norm_dt, norm_gdt)]
+               ParamSpec(p + "down_proj", ffn * h, mat_dt, mat_gdt)]
     ps += [ParamSpec("norm", h, norm_dt, norm_gdt), ParamSpec("lm_head", vocab * h, mat_dt, mat_gdt)]
     return ps
 

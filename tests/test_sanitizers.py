@@ -8,6 +8,11 @@ also runs three steps (one overflowing), a state export / import, the local
 reduce and the bucket check on the small ones.  Each driver is built twice
 with the host compiler, plainly and with the sanitizers (no recovery); the
 sanitized run must end cleanly and print exactly what the plain build prints.
+
+The oracle's range functions, which the GPU parity harness calls from many
+host threads at once, also run from 8 threads under ThreadSanitizer
+(tests/sanitize/oracle_threads.c): no race may be reported, and the combined
+results must equal the same ranges run on one thread.
 """
 import os
 import random
@@ -110,3 +115,27 @@ def test_oracle_under_sanitizers(tmp_path, cases):
     n_num = a.count("\nexport ")
     assert n_num >= 20 and a.count("overflow ok") == n_num and "BAD" not in a
     assert a.count(" same 1\n") == n_num  # import of an export leaves the state unchanged
+
+
+def _threads_cmd(tmp, name, extra):
+    od = os.path.join(ROOT, "oracle")
+    return ["gcc", "-std=c11", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", *extra, "-I", od,
+            os.path.join(od, "oracle.c"), os.path.join(ROOT, "tests", "sanitize", "oracle_threads.c"), "-lm",
+            "-pthread", "-o", os.path.join(tmp, name)]
+
+
+@pytest.mark.timeout(600)
+def test_oracle_ranges_from_threads_under_tsan(tmp_path):
+    tmp = str(tmp_path)
+    plain = _build(tmp, "threads_plain", _threads_cmd(tmp, "threads_plain", []))
+    tsan = _build(tmp, "threads_tsan", _threads_cmd(tmp, "threads_tsan", ["-fsanitize=thread"]))
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:exitcode=66")
+    r = subprocess.run([tsan], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
+    a = subprocess.run([plain], capture_output=True, text=True, timeout=300)
+    assert a.returncode == 0 and a.stdout == r.stdout
+    lines = r.stdout.splitlines()
+    assert len(lines) == 6
+    for par, ser in zip(lines[0::2], lines[1::2]):
+        assert par.startswith("threads") and ser.startswith("serial")
+        assert par.split(None, 1)[1] == ser.split(None, 1)[1]  # bit-identical combined results
