@@ -400,7 +400,7 @@ def main():
     if args.warmup is None:
         args.warmup = 200 if small else 3
     D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
-    bufs_c = D.tensors(A.bufs)
+    bufs_c = D.tensors(L, A.bufs)
     hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
     if args.mode == "reduce":
         bench_reduce(args, w, L, A, bufs_c, hp_c, stream)

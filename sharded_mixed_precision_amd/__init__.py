@@ -177,6 +177,35 @@ def _addr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+DOPT_ERR_INVALID = -1
+_TORCH_DTYPE_NAMES = {"f32": "torch.float32", "bf16": "torch.bfloat16", "f16": "torch.float16"}
+
+
+def _dev(x, what: str, dtype: Optional[str] = None, min_numel: int = 0, min_bytes: int = 0) -> int:
+    """Device address of ``x`` after checking it against what the library
+    will touch: a contiguous device tensor of the given element type holding
+    at least ``min_numel`` elements / ``min_bytes`` bytes.  The library cannot
+    check sizes itself (it receives bare pointers), and a short buffer would
+    make its kernels read or write past the end.  A raw integer address is
+    passed through: its size and type are then the caller's to guarantee."""
+    if x is None:
+        raise DoptError(DOPT_ERR_INVALID, f"{what}: missing")
+    if isinstance(x, int):
+        return x
+    if dtype is not None and str(x.dtype) != _TORCH_DTYPE_NAMES[dtype]:
+        raise DoptError(DOPT_ERR_INVALID, f"{what}: dtype {x.dtype}, the layout needs {_TORCH_DTYPE_NAMES[dtype]}")
+    if x.numel() < min_numel:
+        raise DoptError(DOPT_ERR_INVALID, f"{what}: {x.numel()} elements, the layout needs at least {min_numel}")
+    if x.numel() * x.element_size() < min_bytes:
+        raise DoptError(DOPT_ERR_INVALID,
+                        f"{what}: {x.numel() * x.element_size()} bytes, the layout needs at least {min_bytes}")
+    if not x.is_contiguous():
+        raise DoptError(DOPT_ERR_INVALID, f"{what}: not contiguous")
+    if not getattr(x, "is_cuda", False):
+        raise DoptError(DOPT_ERR_INVALID, f"{what}: not a device tensor")
+    return x.data_ptr()
+
+
 def _stream(s) -> Optional[int]:
     if s is None:
         return None
@@ -206,6 +235,17 @@ class Layout:
     @property
     def num_buffers(self) -> int:
         return int(_lib.dopt_layout_num_buffers(self._h))
+
+    def infos(self) -> List[Dict]:
+        """dopt_layout_buffer of every buffer, with the dtype names (cached;
+        the layout is immutable)."""
+        if getattr(self, "_infos", None) is None:
+            out = []
+            for k in range(self.num_buffers):
+                b = self.buffer(k)
+                out.append({**b, "pd": DTYPE_NAMES[b["param_dtype"]], "gd": DTYPE_NAMES[b["grad_dtype"]]})
+            self._infos = out
+        return self._infos
 
     def sharding(self) -> Dict:
         o = dopt_sharding_info()
@@ -275,15 +315,47 @@ def dopt_build_ranges(params: Sequence, dp_size: int, dp_rank: int, bucket_size:
     return Layout(h, dp_size, dp_rank, n)
 
 
-def _tensors(bufs: Sequence[Dict]) -> ctypes.Array:
+class Tensors:
+    """The device arrays of every flat buffer, checked against one layout and
+    marshalled into the C array of dopt_buffer_tensors (make it once with
+    tensors() and pass it to every step)."""
+
+    def __init__(self, layout: "Layout", arr: ctypes.Array, need_grad: bool):
+        self.handle, self.arr, self.need_grad = layout.handle.value, arr, need_grad
+
+
+def tensors(layout: "Layout", bufs: Sequence[Dict], need_grad: bool = True) -> Tensors:
+    """bufs: per flat buffer a dict with grad, param, master (None for fp32
+    params), exp_avg and exp_avg_sq, each of the buffer's arena_numel
+    elements: device tensors (checked here) or raw device addresses."""
+    infos = layout.infos()
+    if len(bufs) != len(infos):
+        raise DoptError(DOPT_ERR_INVALID, f"{len(bufs)} buffer entries, the layout has {len(infos)}")
     arr = (dopt_buffer_tensors * len(bufs))()
-    for k, b in enumerate(bufs):
-        arr[k].grad = _addr(b.get("grad"))
-        arr[k].param = _addr(b.get("param"))
-        arr[k].master = _addr(b.get("master"))
-        arr[k].exp_avg = _addr(b.get("exp_avg"))
-        arr[k].exp_avg_sq = _addr(b.get("exp_avg_sq"))
-    return arr
+    for k, (b, inf) in enumerate(zip(bufs, infos)):
+        n, pre = inf["arena_numel"], f"buffer {k} "
+        if need_grad or b.get("grad") is not None:
+            arr[k].grad = _dev(b.get("grad"), pre + "grad", inf["gd"], n)
+        arr[k].param = _dev(b.get("param"), pre + "param", inf["pd"], n)
+        if inf["pd"] != "f32":
+            arr[k].master = _dev(b.get("master"), pre + "master", "f32", n)
+        arr[k].exp_avg = _dev(b.get("exp_avg"), pre + "exp_avg", "f32", n)
+        arr[k].exp_avg_sq = _dev(b.get("exp_avg_sq"), pre + "exp_avg_sq", "f32", n)
+    return Tensors(layout, arr, need_grad)
+
+
+def _marshal(layout: "Layout", bufs, need_grad: bool = True) -> ctypes.Array:
+    if isinstance(bufs, Tensors):
+        if bufs.handle != layout.handle.value:
+            raise DoptError(DOPT_ERR_INVALID, "tensors were marshalled for another layout")
+        if need_grad and not bufs.need_grad:
+            raise DoptError(DOPT_ERR_INVALID, "tensors were marshalled without grads")
+        return bufs.arr
+    return tensors(layout, bufs, need_grad).arr
+
+
+def _ws(layout: "Layout", workspace) -> int:
+    return _dev(workspace, "workspace", None, 0, layout.workspace_bytes)
 
 
 def scaler_cfg(dynamic: bool = False, initial_scale: float = 1.0, growth_factor: float = 2.0,
@@ -301,39 +373,44 @@ def _hparams(hps: Sequence) -> ctypes.Array:
 
 
 def dopt_init_state(layout: Layout, bufs: Sequence[Dict], scaler: dopt_scaler_cfg, workspace, stream=None):
-    _check(_lib.dopt_init_state(layout.handle, _tensors(bufs), ctypes.byref(scaler), _addr(workspace),
-                                _stream(stream)))
+    _check(_lib.dopt_init_state(layout.handle, _marshal(layout, bufs, False), ctypes.byref(scaler),
+                                _ws(layout, workspace), _stream(stream)))
 
 
 def dopt_step(layout: Layout, bufs, hparams: Sequence, max_grad_norm: float, workspace, stream=None,
-              want_stats: bool = True, _tensors_cache=None):
+              want_stats: bool = True):
     st = dopt_stats() if want_stats else None
-    t = _tensors_cache if _tensors_cache is not None else (bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs))
+    t = _marshal(layout, bufs)
     hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
-    _check(_lib.dopt_step(layout.handle, t, hp, len(hparams), max_grad_norm, _addr(workspace), _stream(stream),
-                          ctypes.byref(st) if st is not None else None))
+    _check(_lib.dopt_step(layout.handle, t, hp, len(hparams), max_grad_norm, _ws(layout, workspace),
+                          _stream(stream), ctypes.byref(st) if st is not None else None))
     return st.as_dict() if st is not None else None
 
 
 def dopt_step_prepare(layout: Layout, bufs, hparams, max_grad_norm: float, workspace, stream=None):
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
+    t = _marshal(layout, bufs)
     hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
-    _check(_lib.dopt_step_prepare(layout.handle, t, hp, len(hp), max_grad_norm, _addr(workspace), _stream(stream)))
+    _check(_lib.dopt_step_prepare(layout.handle, t, hp, len(hp), max_grad_norm, _ws(layout, workspace),
+                                  _stream(stream)))
 
 
 def dopt_reduce_prepare(layout: Layout, bufs, chunks: Sequence, wire_dtype: str, n_chunks: int, scale: float,
                         hparams, max_grad_norm: float, workspace, stream=None):
     """chunks: one device buffer per flat buffer holding n_chunks arenas back to back.
     hparams None: stats only (finalize later with dopt_step_finalize)."""
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
-    ch = (ctypes.c_void_p * len(chunks))(*[_addr(c) for c in chunks])
+    t = _marshal(layout, bufs)
+    infos = layout.infos()
+    if len(chunks) != len(infos):
+        raise DoptError(DOPT_ERR_INVALID, f"{len(chunks)} chunk buffers, the layout has {len(infos)}")
+    ch = (ctypes.c_void_p * len(chunks))(*[_dev(c, f"buffer {k} chunks", wire_dtype, n_chunks * inf["arena_numel"])
+                                            for k, (c, inf) in enumerate(zip(chunks, infos))])
     if hparams is None:
         hp, nh = None, 0
     else:
         hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
         nh = len(hp)
     _check(_lib.dopt_reduce_prepare(layout.handle, t, ch, DTYPES[wire_dtype], n_chunks, scale, hp, nh,
-                                    max_grad_norm, _addr(workspace), _stream(stream)))
+                                    max_grad_norm, _ws(layout, workspace), _stream(stream)))
 
 
 class dopt_bucket_check(ctypes.Structure):
@@ -346,8 +423,12 @@ BUCKET_CHECK_BYTES = ctypes.sizeof(dopt_bucket_check)
 
 def dopt_check_grads(layout: Layout, k: int, grad_buffer, large_threshold: float, out, workspace, stream=None):
     """out: device buffer of n_buckets * BUCKET_CHECK_BYTES bytes (e.g. a uint8 CUDA tensor)."""
-    _check(_lib.dopt_check_grads(layout.handle, k, _addr(grad_buffer), large_threshold, _addr(out),
-                                 _addr(workspace), _stream(stream)))
+    infos = layout.infos()
+    if not 0 <= k < len(infos):
+        raise DoptError(-5, f"buffer index {k} out of range")
+    g = _dev(grad_buffer, f"buffer {k} grad buffer", infos[k]["gd"], infos[k]["numel"])
+    o = _dev(out, "bucket check output", None, 0, infos[k]["n_buckets"] * BUCKET_CHECK_BYTES)
+    _check(_lib.dopt_check_grads(layout.handle, k, g, large_threshold, o, _ws(layout, workspace), _stream(stream)))
 
 
 def bucket_checks(raw: bytes, n: int) -> List[Dict]:
@@ -357,55 +438,57 @@ def bucket_checks(raw: bytes, n: int) -> List[Dict]:
 
 
 def dopt_step_stats(layout: Layout, bufs, workspace, stream=None):
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
-    _check(_lib.dopt_step_stats(layout.handle, t, _addr(workspace), _stream(stream)))
+    t = _marshal(layout, bufs)
+    _check(_lib.dopt_step_stats(layout.handle, t, _ws(layout, workspace), _stream(stream)))
 
 
 def dopt_step_finalize(layout: Layout, hparams, max_grad_norm: float, workspace, stream=None):
     hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
-    _check(_lib.dopt_step_finalize(layout.handle, hp, len(hp), max_grad_norm, _addr(workspace), _stream(stream)))
+    _check(_lib.dopt_step_finalize(layout.handle, hp, len(hp), max_grad_norm, _ws(layout, workspace),
+                                   _stream(stream)))
 
 
 def dopt_step_apply(layout: Layout, bufs, workspace, stream=None):
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
-    _check(_lib.dopt_step_apply(layout.handle, t, _addr(workspace), _stream(stream)))
+    t = _marshal(layout, bufs)
+    _check(_lib.dopt_step_apply(layout.handle, t, _ws(layout, workspace), _stream(stream)))
 
 
 def dopt_read_stats(layout: Layout, workspace, stream=None) -> Dict:
     st = dopt_stats()
-    _check(_lib.dopt_read_stats(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
+    _check(_lib.dopt_read_stats(layout.handle, _ws(layout, workspace), _stream(stream), ctypes.byref(st)))
     return st.as_dict()
 
 
 def dopt_state_export(layout: Layout, bufs, master, exp_avg, exp_avg_sq, workspace, stream=None):
     """Write the rank's (master, m, v) shards in model order into three fp32
     device arrays of layout.state_numel() elements."""
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
-    _check(_lib.dopt_state_export(layout.handle, t, _addr(master), _addr(exp_avg), _addr(exp_avg_sq),
-                                  _addr(workspace), _stream(stream)))
+    t = _marshal(layout, bufs, False)
+    x = [_dev(a, f"export {name}", "f32", layout.state_numel)
+         for a, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"))]
+    _check(_lib.dopt_state_export(layout.handle, t, *x, _ws(layout, workspace), _stream(stream)))
 
 
 def dopt_state_import(layout: Layout, bufs, master, exp_avg, exp_avg_sq, workspace, stream=None):
     """Inverse of dopt_state_export; also rewrites the param window from the master."""
-    t = bufs if isinstance(bufs, ctypes.Array) else _tensors(bufs)
-    _check(_lib.dopt_state_import(layout.handle, t, _addr(master), _addr(exp_avg), _addr(exp_avg_sq),
-                                  _addr(workspace), _stream(stream)))
+    t = _marshal(layout, bufs, False)
+    x = [_dev(a, f"import {name}", "f32", layout.state_numel)
+         for a, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"))]
+    _check(_lib.dopt_state_import(layout.handle, t, *x, _ws(layout, workspace), _stream(stream)))
 
 
 def dopt_state_scalars_get(layout: Layout, workspace, stream=None) -> Dict:
     st = dopt_state_scalars()
-    _check(_lib.dopt_state_scalars_get(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
+    _check(_lib.dopt_state_scalars_get(layout.handle, _ws(layout, workspace), _stream(stream), ctypes.byref(st)))
     return {name: getattr(st, name) for name, _ in st._fields_}
 
 
 def dopt_state_scalars_set(layout: Layout, workspace, scalars: Dict, stream=None):
     st = dopt_state_scalars(**scalars)
-    _check(_lib.dopt_state_scalars_set(layout.handle, _addr(workspace), _stream(stream), ctypes.byref(st)))
+    _check(_lib.dopt_state_scalars_set(layout.handle, _ws(layout, workspace), _stream(stream), ctypes.byref(st)))
 
 
 def dopt_last_error() -> str:
     return _lib.dopt_last_error().decode()
 
 
-tensors = _tensors
 hparams_array = _hparams

@@ -76,7 +76,7 @@ class DeviceArenas:
         from . import dopt_init_state, dopt_step_apply, dopt_step_prepare, hparams_array, scaler_cfg, tensors
         stream = torch.cuda.current_stream()
         dopt_init_state(self.layout, bufs, scaler_cfg(False, 1.0), ws, stream)
-        t = tensors(bufs)
+        t = tensors(self.layout, bufs)
         hp = hparams_array([(1e-3, 0.9, 0.999, 1e-8, 0.0)] * DOPT_MAX_HGROUPS)
         dopt_step_prepare(self.layout, t, hp, 0.0, ws, stream)
         dopt_step_apply(self.layout, t, ws, stream)

@@ -1,0 +1,121 @@
+"""The Python binding refuses, before any library call, device arrays that do
+not match the layout: a wrong element type, too few elements, a
+non-contiguous view, a host tensor, a missing array, a workspace that is too
+small, tensors marshalled for another layout.  The C library receives bare
+pointers and cannot check sizes itself, so a short array would make its
+kernels read or write past its end.  Runs on the CPU: every check fires
+before anything touches a device."""
+import pytest
+import torch
+
+import sharded_mixed_precision_amd as D
+from synth.models import ParamSpec
+
+PARAMS = [ParamSpec("w", 5000, "bf16", "f32"), ParamSpec("n", 300, "f32", "f32"), ParamSpec("h", 7000, "f16", "f16")]
+
+
+@pytest.fixture(scope="module")
+def L():
+    return D.dopt_build_ranges(PARAMS, 4, 1, 0)
+
+
+T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _bufs(L, **override):
+    """Raw device addresses (which pass: their size is the caller's to
+    guarantee) for every array, with the given entries replaced."""
+    out = []
+    for inf in L.infos():
+        out.append({"grad": 4096, "param": 4096, "master": 4096 if inf["pd"] != "f32" else None,
+                    "exp_avg": 4096, "exp_avg_sq": 4096})
+    for key, val in override.items():
+        k, name = key.split("_", 1)
+        out[int(k[1:])][name] = val
+    return out
+
+
+def _err(fn, *words):
+    with pytest.raises(D.DoptError) as e:
+        fn()
+    for w in words:
+        assert w in str(e.value), str(e.value)
+    assert e.value.code == -1 or e.value.code == -5
+
+
+def test_layout_infos(L):
+    inf = L.infos()
+    assert [(i["pd"], i["gd"]) for i in inf] == [("bf16", "f32"), ("f32", "f32"), ("f16", "f16")]
+    assert all(i["arena_numel"] % D.DOPT_ARENA_ALIGN == 0 for i in inf)
+
+
+def test_host_tensors_of_the_right_shape_are_refused_as_host_memory(L):
+    inf = L.infos()[2]
+    n = inf["arena_numel"]
+    _err(lambda: D.tensors(L, _bufs(L, b2_grad=torch.zeros(n, dtype=torch.float16))), "buffer 2 grad",
+         "not a device tensor")
+    _err(lambda: D.tensors(L, _bufs(L, b2_master=torch.zeros(n))), "buffer 2 master", "not a device tensor")
+    D.tensors(L, _bufs(L))
+
+
+def test_wrong_dtype(L):
+    n = L.infos()[0]["arena_numel"]
+    _err(lambda: D.tensors(L, _bufs(L, b0_grad=torch.zeros(n, dtype=torch.bfloat16))), "buffer 0 grad", "dtype")
+    _err(lambda: D.tensors(L, _bufs(L, b2_param=torch.zeros(n, dtype=torch.bfloat16))), "buffer 2 param", "dtype")
+    _err(lambda: D.tensors(L, _bufs(L, b0_exp_avg=torch.zeros(n, dtype=torch.float64))), "exp_avg", "dtype")
+
+
+def test_too_short(L):
+    n = L.infos()[1]["arena_numel"]
+    _err(lambda: D.tensors(L, _bufs(L, b1_exp_avg_sq=torch.zeros(n - 1))), "buffer 1 exp_avg_sq", "at least")
+    _err(lambda: D.tensors(L, _bufs(L, b0_master=torch.zeros(10))), "buffer 0 master", "at least")
+
+
+def test_non_contiguous(L):
+    n = L.infos()[0]["arena_numel"]
+    strided = torch.zeros(2 * n)[::2]
+    _err(lambda: D.tensors(L, _bufs(L, b0_exp_avg=strided)), "not contiguous")
+
+
+def test_missing_arrays_and_buffer_count(L):
+    _err(lambda: D.tensors(L, _bufs(L, b0_master=None)), "buffer 0 master", "missing")
+    _err(lambda: D.tensors(L, _bufs(L, b2_grad=None)), "buffer 2 grad", "missing")
+    _err(lambda: D.tensors(L, _bufs(L)[:2]), "2 buffer entries")
+    # fp32 params are their own master: none is needed there
+    D.tensors(L, _bufs(L, b1_master=None))
+
+
+def test_workspace_and_marshalled_tensors(L):
+    raw = _bufs(L)
+    t = D.tensors(L, raw)
+    small_ws = torch.zeros(L.workspace_bytes - 1, dtype=torch.uint8)
+    _err(lambda: D.dopt_step_apply(L, t, small_ws), "workspace", "bytes")
+    other = D.dopt_build_ranges(PARAMS, 4, 2, 0)
+    _err(lambda: D.dopt_step_apply(other, t, 0), "another layout")
+    t_nograd = D.tensors(L, [{**b, "grad": None} for b in raw], need_grad=False)
+    _err(lambda: D.dopt_step(L, t_nograd, [(1e-3, 0.9, 0.999, 1e-8, 0.0)], 1.0, 0), "without grads")
+
+
+def test_bucket_check_needs_the_whole_buffer(L):
+    inf = L.infos()[0]
+    out = torch.zeros(inf["n_buckets"] * D.BUCKET_CHECK_BYTES, dtype=torch.uint8)
+    arena_grad = torch.zeros(inf["arena_numel"], dtype=torch.float32)  # the rank's window, not the buffer
+    assert inf["arena_numel"] < inf["numel"]
+    _err(lambda: D.dopt_check_grads(L, 0, arena_grad, 1.0, out, 0), "grad buffer", "at least")
+    full = torch.zeros(inf["numel"], dtype=torch.float32)
+    _err(lambda: D.dopt_check_grads(L, 0, 4096, 1.0, out[:-1], 0), "bucket check output", "bytes")
+    _err(lambda: D.dopt_check_grads(L, 3, full, 1.0, out, 0), "out of range")
+
+
+def test_reduce_chunks_and_exports(L):
+    t = D.tensors(L, _bufs(L))
+    infos = L.infos()
+    ch = [torch.zeros(4 * inf["arena_numel"], dtype=torch.bfloat16) for inf in infos]
+    ch[0] = 4096  # a raw address passes
+    ch[1] = torch.zeros(3 * infos[1]["arena_numel"], dtype=torch.bfloat16)
+    _err(lambda: D.dopt_reduce_prepare(L, t, ch, "bf16", 4, 1.0, None, 1.0, 0), "buffer 1 chunks", "at least")
+    _err(lambda: D.dopt_reduce_prepare(L, t, ch[:2], "bf16", 4, 1.0, None, 1.0, 0), "2 chunk buffers")
+    n = L.state_numel
+    ok, short = torch.zeros(n), torch.zeros(n - 1)
+    _err(lambda: D.dopt_state_export(L, t, 4096, short, ok, 0), "export exp_avg", "at least")
+    _err(lambda: D.dopt_state_import(L, t, ok.double(), ok, ok, 0), "import master", "dtype")

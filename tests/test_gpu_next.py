@@ -97,5 +97,5 @@ def test_reduce_argument_errors():
     A2 = DeviceArenas(L2)
     D.dopt_init_state(L2, A2.bufs, D.scaler_cfg(), A2.workspace, stream)
     with pytest.raises(D.DoptError):  # not with more than one optimizer instance
-        D.dopt_reduce_prepare(L2, A2.bufs, [torch.zeros(2 * A2.info[0]["n"], dtype=torch.bfloat16, device="cuda")],
+        D.dopt_reduce_prepare(L2, A2.bufs, [torch.zeros(4 * A2.info[0]["n"], dtype=torch.bfloat16, device="cuda")],
                               "bf16", 4, 1.0, hp, 1.0, A2.workspace, stream)

@@ -219,8 +219,11 @@ def test_argument_errors_are_reported():
         D.dopt_step(L, A.bufs, [(1e-3, 0.9, 0.999, 1e-8, 0.0)], 1.0, A.workspace, stream)
     assert e.value.code == -1
     bad = dict(A.bufs[0])
-    bad["grad"] = A.bufs[0]["grad"][1:]  # 2-byte offset: not 256-byte aligned
-    with pytest.raises(D.DoptError):
+    bad["grad"] = A.bufs[0]["grad"].data_ptr() + 2  # a raw address 2 bytes off: not 256-byte aligned (the library)
+    with pytest.raises(D.DoptError, match="aligned"):
+        D.dopt_step(L, [bad], [(1e-3, 0.9, 0.999, 1e-8, 0.0)] * 2, 1.0, A.workspace, stream)
+    bad["grad"] = A.bufs[0]["grad"][1:]  # one element short (the binding)
+    with pytest.raises(D.DoptError, match="at least"):
         D.dopt_step(L, [bad], [(1e-3, 0.9, 0.999, 1e-8, 0.0)] * 2, 1.0, A.workspace, stream)
     with pytest.raises(D.DoptError):
         D.dopt_init_state(L, A.bufs, D.scaler_cfg(True, 0.0), A.workspace, stream)
