@@ -15,8 +15,15 @@ events' own cost is spread over the batch.  Last, K steps run with the
 256 MB last-level cache flushed before each (`llc_flushed`): back-to-back
 steps of a small window find much of their data still in that cache.
 
-Prints one JSON line.  The default workload is a GPT-2-small-shaped param
-list sharded N=8, rank 3, 40M-element buckets, bf16 params and grads.
+Prints one JSON line.  The headline workload is the dense 7B list at N=1
+(6.74e9 fp16 params with fp16 grads under a dynamic loss scale: the largest
+workload that one GPU holds whole, 202 GB moved per step); the line also
+carries, under "secondary", the GPT-2-small-shaped rank (N=8, rank 3) with its
+step timed back to back and with the last-level cache flushed, and the
+distribution of pass-2 times over the arena placements the start-up search
+tried.  Inputs are seeded draws of PyTorch's device generator (the parity
+tests use the host generator of synth/; the step's speed does not depend on
+the values).
 """
 from __future__ import annotations
 
@@ -47,6 +54,11 @@ MEASURED_TRAFFIC = {
     # both buffers' pass-2 launches of one step (bf16 params with fp32 grads + fp32 norms)
     "llama3-8b": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 30176594637},
 }
+
+
+def progress(msg: str):
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def _src_sha() -> str:
@@ -321,10 +333,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: 500 on windows of up to 64M shard elements, else 10)")
+                    help="timed steps (default: 500 on windows of up to 64M shard elements, else 20)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: 200 on windows of up to 64M shard elements, else 3)")
-    ap.add_argument("--workload", default="gpt2-small")
+    ap.add_argument("--workload", default="dense-7b",
+                    help="the headline workload (default: the 7B dense list at N=1, the largest one-GPU workload)")
+    ap.add_argument("--secondary", default="gpt2-small",
+                    help="step mode: a second workload measured after the first and reported under 'secondary' "
+                         "with its own default step counts ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["step", "reduce", "check", "checkpoint"], default="step",
@@ -348,7 +364,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    progress("importing torch")
     import torch
+    progress(f"torch {torch.__version__}, device {torch.cuda.get_device_name(0) if torch.cuda.is_available() else None}")
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -367,50 +385,131 @@ def main():
                           "ms": round(ms, 5), "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
     import synth
-    import sharded_mixed_precision_amd as D
-    from sharded_mixed_precision_amd.arena import DeviceArenas
 
     w = synth.WORKLOADS[args.workload]
+    if args.mode != "step":
+        run_other_mode(args, w)
+        return
+    res = measure_step(w, args.steps, args.warmup, args.placement_tries, args.flush_llc)
+    out = {
+        "metric": METRIC,
+        "value": res["value"],
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": res["warmup"],
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded draws on the device)",
+        "config": res["config"],
+        "hbm_GBps_step": res["hbm_GBps_step"],
+        "hbm_frac_step": res["hbm_frac_step"],
+        "roofline": res["roofline"],
+    }
+    for key in ("skip_step", "llc_flushed"):
+        if key in res:
+            out[key] = res[key]
+    if args.secondary and args.secondary != args.workload:
+        # the GPT-2-small rank: a window whose 249 MB of step data nearly fits
+        # the 256 MB last-level cache, so its back-to-back figure is
+        # cache-assisted; its flushed figure is the HBM-bound one
+        import torch
+        torch.cuda.empty_cache()
+        sw = synth.WORKLOADS[args.secondary]
+        sec = measure_step(sw, None, None, args.placement_tries, False)
+        out["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "steps", "warmup", "hbm_GBps_step",
+                                                 "hbm_frac_step", "roofline", "llc_flushed")}
+        out["secondary"]["workload"] = sec["config"]["workload"]
+        out["secondary"]["llc"] = "warm (steps back to back): the step's data nearly fits the 256 MB last-level " \
+                                  "cache, so value and roofline are cache-assisted; llc_flushed is HBM-bound"
+    if not args.no_cpu_baseline:
+        progress("oracle CPU baseline")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def fill_device(t, sigma: float, seed: int, scale: float = 1.0, zero_frac: float = 0.0, chunk: int = 1 << 28):
+    """Seeded synthetic values drawn on the device into t: storage(scale *
+    N(0, sigma^2)) by PyTorch's device generator, with exact zeros at the
+    given fraction (an independent uniform draw per element)."""
+    import torch
+    g = torch.Generator(device=t.device)
+    g.manual_seed(seed)
+    for s in range(0, t.numel(), chunk):
+        part = t[s:s + chunk]
+        part.normal_(0.0, sigma * scale, generator=g)
+        if zero_frac > 0.0:
+            part.masked_fill_(torch.rand(part.numel(), device=t.device, generator=g) < zero_frac, 0.0)
+
+
+def setup(w, placement_tries: int):
+    """Layout, arenas (with the placement search) and seeded inputs of one
+    workload, state initialised; returns (L, A, bufs_c, hp_c, sizes, alloc_seconds)."""
+    import torch
+    import sharded_mixed_precision_amd as D
+    import synth
+    from sharded_mixed_precision_amd.arena import DeviceArenas
+
     params = synth.PARAM_LISTS[w.model]()
     L = D.dopt_build_ranges(params, w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
     t_alloc = time.perf_counter()
-    A = DeviceArenas(L, placement_tries=args.placement_tries)
+    A = DeviceArenas(L, placement_tries=placement_tries)
     torch.cuda.synchronize()
     t_alloc = time.perf_counter() - t_alloc
-    stream = torch.cuda.current_stream()
-    E = 0
-    bytes_step = 0
-    apply_bytes = 0
+    sizes = {"E": 0, "bytes_step": 0, "apply_bytes": 0, "n_params": len(params)}
     for k, info in enumerate(A.info):
         p1, p2 = pass_bytes(info["pd"], info["gd"])
-        E += info["shard_numel"]
-        bytes_step += (p1 + p2) * info["shard_numel"]
-        apply_bytes += p2 * info["shard_numel"]
-        A.bufs[k]["param"].copy_(synth.fill_normal(info["pd"], info["n"], w.seed, synth.weight_stream(k), 0,
-                                                   w.weight_sigma))
-        A.bufs[k]["grad"].copy_(synth.fill_normal(info["gd"], info["n"], w.seed, synth.grad_stream(k), 1,
-                                                  w.grad_sigma, scale=w.initial_scale, zero_frac=w.zero_frac))
+        sizes["E"] += info["shard_numel"]
+        sizes["bytes_step"] += (p1 + p2) * info["shard_numel"]
+        sizes["apply_bytes"] += p2 * info["shard_numel"]
+        fill_device(A.bufs[k]["param"], w.weight_sigma, 1_000_003 * w.seed + 2 * k)
+        fill_device(A.bufs[k]["grad"], w.grad_sigma, 1_000_003 * w.seed + 2 * k + 1, w.initial_scale, w.zero_frac)
+    stream = torch.cuda.current_stream()
+    D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
+    bufs_c = D.tensors(L, A.bufs)
+    hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
+    return L, A, bufs_c, hp_c, sizes, t_alloc
+
+
+def placement_summary(A, seconds: float) -> dict:
+    """The distribution of pass-2 times over the placements the search tried:
+    whole arena sets, then each array's candidates with the others fixed."""
+    import statistics
+    p = A.placement
+    if p is None:
+        return {"candidates": 1, "seconds": round(seconds, 3)}
+    whole = p["pass2_ms"]
+    out = {"whole_sets": {"n": len(whole), "kept_ms": whole[p["kept"]], "median_ms": round(statistics.median(whole), 4),
+                          "worst_ms": max(whole), "all_ms": whole},
+           "per_array": [], "seconds": round(seconds, 3)}
+    for k, key, n, ms_list in p["refined"]:
+        out["per_array"].append({"array": f"{k}.{key}", "n": len(ms_list), "kept_ms": min(ms_list),
+                                 "median_ms": round(statistics.median(ms_list), 4), "worst_ms": max(ms_list)})
+    out["kept_pass2_ms"] = min(p["refined"][-1][3]) if p["refined"] else whole[p["kept"]]
+    return out
+
+
+def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool) -> dict:
+    """Time K back-to-back steps of one workload (or K steps each after an
+    LLC flush), then pass 2 on its own, the flushed steps, and the skipped
+    step for a dynamically scaled workload."""
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    L, A, bufs_c, hp_c, sz, t_alloc = setup(w, placement_tries)
+    stream = torch.cuda.current_stream()
+    E, bytes_step, apply_bytes = sz["E"], sz["bytes_step"], sz["apply_bytes"]
+    progress(f"{w.name}: arenas placed in {t_alloc:.1f}s, inputs drawn, state initialised")
     # A small window's step lasts tens of microseconds: hundreds of warm-up
     # steps let the clocks settle, and hundreds of timed steps keep the timed
     # region in the tens of milliseconds.  A large window's step lasts
     # milliseconds.
     small = E <= SMALL_WINDOW
-    if args.steps is None:
-        args.steps = 500 if small else 10
-    if args.warmup is None:
-        args.warmup = 200 if small else 3
-    D.dopt_init_state(L, A.bufs, D.scaler_cfg(w.dynamic_scale, w.initial_scale), A.workspace, stream)
-    bufs_c = D.tensors(L, A.bufs)
-    hp_c = D.hparams_array([(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)])
-    if args.mode == "reduce":
-        bench_reduce(args, w, L, A, bufs_c, hp_c, stream)
-        return
-    if args.mode == "check":
-        bench_check(args, w, L, A, stream)
-        return
-    if args.mode == "checkpoint":
-        bench_checkpoint(args, w, L, A, bufs_c, stream)
-        return
+    K = steps if steps is not None else (500 if small else 20)
+    W = warmup if warmup is not None else (200 if small else 3)
 
     def step():
         D.dopt_step(L, bufs_c, hp_c, w.max_grad_norm, A.workspace, stream, want_stats=False)
@@ -424,10 +523,9 @@ def main():
             D.dopt_step_apply(L, bufs_c, A.workspace, stream)
         ev_b.record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(W):
         step()
     torch.cuda.synchronize()
-    K = args.steps
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
@@ -444,7 +542,7 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in zip(ev_s, ev_e))
 
-    if args.flush_llc:
+    if flush_llc:
         total_ms = flushed_steps()
     else:
         t_start = torch.cuda.Event(enable_timing=True)
@@ -459,42 +557,31 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for i in range(K):
-        if args.flush_llc:
+        if flush_llc:
             flush.fill_(i & 0xff)
         step_bracketed(ev_a[i], ev_b[i])
     torch.cuda.synchronize()
     apply_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / (K * APPLY_BATCH)
+    progress(f"{w.name}: {K} steps at {total_ms / K:.4f} ms, pass 2 at {apply_ms:.4f} ms")
     # the same steps with the last-level cache flushed before each (reported
     # beside the back-to-back figure; a training step runs after forward and
     # backward have passed far more than 256 MB through the cache)
-    flushed_ms = None if args.flush_llc else flushed_steps() / K
+    flushed_ms = None if flush_llc else flushed_steps() / K
     st = D.dopt_read_stats(L, A.workspace, stream)
-    assert st["skipped"] == 0 and st["step_count"] == args.warmup + (2 if args.flush_llc else 3) * K, st
+    assert st["skipped"] == 0 and st["step_count"] == W + (2 if flush_llc else 3) * K, st
     skip = skip_step(L, A, step, K, stream) if w.dynamic_scale else None
     ms = total_ms / K
-    value = E / (ms * 1e-3) / 1e9
     gbps = bytes_step / (ms * 1e-3) / 1e9
     ach = apply_bytes / (apply_ms * 1e-3) / 1e9
-    tr = MEASURED_TRAFFIC.get(args.workload)
+    tr = MEASURED_TRAFFIC.get(w.name)
     traffic = tr["bytes_per_launch"] if tr and tr.get("src") == _src_sha() else None
-    out = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "Gparams/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"{w.name}: {len(params)}-param list, rank {w.dp_rank} of N={w.dp_size}, "
+    res = {
+        "value": round(E / (ms * 1e-3) / 1e9, 3), "steps": K, "warmup": W, "ms_per_step": round(ms, 5),
+        "config": {"workload": f"{w.name}: {sz['n_params']}-param list, rank {w.dp_rank} of N={w.dp_size}, "
                                f"bucket {w.bucket_size}, {E} shard elements",
                    "shard_elements": E, "bytes_per_step": bytes_step,
-                   "llc": "flushed before each step" if args.flush_llc else "warm (steps back to back)",
-                   "arena_placement": {**(A.placement or {"candidates": 1}), "seconds": round(t_alloc, 3)}},
+                   "llc": "flushed before each step" if flush_llc else "warm (steps back to back)",
+                   "arena_placement": placement_summary(A, t_alloc)},
         "hbm_GBps_step": round(gbps, 1),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),
@@ -503,13 +590,31 @@ def main():
                      "algorithmic_bytes_per_launch": apply_bytes},
     }
     if skip is not None:
-        out["skip_step"] = skip
+        res["skip_step"] = skip
     if flushed_ms is not None:
-        out["llc_flushed"] = {"ms_per_step": round(flushed_ms, 5), "value": round(E / (flushed_ms * 1e-3) / 1e9, 3),
-                              "unit": "Gparams/s", "hbm_GBps_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9, 1)}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+        res["llc_flushed"] = {"ms_per_step": round(flushed_ms, 5), "value": round(E / (flushed_ms * 1e-3) / 1e9, 3),
+                              "unit": "Gparams/s", "hbm_GBps_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9, 1),
+                              "hbm_frac_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del A, bufs_c, flush
+    return res
+
+
+def run_other_mode(args, w):
+    import torch
+    import sharded_mixed_precision_amd as D
+
+    L, A, bufs_c, hp_c, sz, _ = setup(w, args.placement_tries)
+    stream = torch.cuda.current_stream()
+    if args.steps is None:
+        args.steps = 50 if sz["E"] <= SMALL_WINDOW else 10
+    if args.warmup is None:
+        args.warmup = 10 if sz["E"] <= SMALL_WINDOW else 2
+    if args.mode == "reduce":
+        bench_reduce(args, w, L, A, bufs_c, hp_c, stream)
+    elif args.mode == "check":
+        bench_check(args, w, L, A, stream)
+    else:
+        bench_checkpoint(args, w, L, A, bufs_c, stream)
 
 
 if __name__ == "__main__":

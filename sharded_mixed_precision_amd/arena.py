@@ -127,6 +127,7 @@ class DeviceArenas:
                 if cur is None:
                     continue
                 best_t, best_ms = cur, self._pass2_ms(bufs, ws, launches)
+                times = [best_ms]
                 free, _ = torch.cuda.mem_get_info()
                 nbytes = cur.numel() * cur.element_size()
                 n = max(0, min(tries, int(0.9 * free) // max(nbytes, 1)))
@@ -135,12 +136,15 @@ class DeviceArenas:
                     held.append(torch.zeros_like(cur))
                     bufs[k][key] = held[-1]
                     ms = self._pass2_ms(bufs, ws, launches)
+                    times.append(ms)
                     if ms < best_ms:
                         best_t, best_ms = held[-1], ms
                 bufs[k][key] = best_t
                 held.clear()
                 cur = None
-                steps.append([k, key, n, round(best_ms, 4)])
+                # [buffer, array, candidates tried, pass-2 ms of the current
+                # array then of each candidate]
+                steps.append([k, key, n, [round(x, 4) for x in times]])
                 torch.cuda.synchronize()
                 torch.cuda.empty_cache()
         return steps

@@ -36,3 +36,25 @@ def test_traffic_is_reported_only_for_the_measured_source():
 def test_cpu_baseline_host_description():
     h = bench.host_cpu()
     assert h["cores_available"] >= 1 and isinstance(h["model"], str) and h["model"]
+
+
+def test_placement_summary_reports_the_distribution():
+    class A:
+        placement = {"candidates": 3, "pass2_ms": [5.9, 5.1, 6.2], "kept": 1,
+                     "refined": [[0, "grad", 2, [5.1, 5.3, 5.0]], [0, "param", 1, [5.0, 5.4]]]}
+    out = bench.placement_summary(A, 3.25)
+    assert out["whole_sets"] == {"n": 3, "kept_ms": 5.1, "median_ms": 5.9, "worst_ms": 6.2, "all_ms": [5.9, 5.1, 6.2]}
+    assert out["per_array"][0] == {"array": "0.grad", "n": 3, "kept_ms": 5.0, "median_ms": 5.1, "worst_ms": 5.3}
+    assert out["kept_pass2_ms"] == 5.0 and out["seconds"] == 3.25
+
+    class B:
+        placement = None
+    assert bench.placement_summary(B, 1.0) == {"candidates": 1, "seconds": 1.0}
+
+
+def test_default_workload_is_the_largest_one_gpu_workload():
+    import synth
+    ap_default = [line for line in open(os.path.join(ROOT, "bench.py")) if '"--workload", default=' in line]
+    assert ap_default and '"dense-7b"' in ap_default[0]
+    w = synth.WORKLOADS["dense-7b"]
+    assert w.dp_size == 1  # the whole model's state on one GPU
