@@ -23,7 +23,8 @@
  *     abort crosses the ABI.
  *   - "host" pointers are CPU memory, "device" pointers are GPU memory
  *     (e.g. from hipMalloc or a PyTorch CUDA tensor).  The library never
- *     allocates or frees device memory.
+ *     allocates or frees device memory; its one device array of its own is
+ *     the fixed static scratch of dopt_check_grads_noalloc.
  *   - Device work is enqueued on the caller's HIP stream and is ordered with
  *     the caller's other work on that stream; nothing synchronizes unless a
  *     function says so.
@@ -368,6 +369,33 @@ typedef struct dopt_bucket_check {
  */
 int dopt_check_grads(const dopt_layout *layout, int32_t k, const void *grad_buffer, double large_threshold,
                      dopt_bucket_check *out, void *workspace, hipStream_t stream);
+
+/* Bytes of the library's static device scratch (see dopt_check_grads_noalloc). */
+#define DOPT_NOALLOC_SCRATCH_BYTES 16777216
+
+/*
+ * dopt_check_grads_noalloc -- dopt_check_grads for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same scan, the same kernels and
+ * bit-identical results, with no workspace argument and no dopt_init_state
+ * needed.  Its bucket table and per-check-tile partials live in a static
+ * device array of DOPT_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU the
+ * library runs on holds until the process ends; the call allocates and frees
+ * nothing, copies nothing from the host (the bucket table travels in kernel
+ * arguments) and does not synchronize.
+ *
+ * A buffer needs 16 bytes per 16384-element check tile plus 24 bytes per
+ * bucket (256-byte aligned): up to about 17e9 elements.  Larger buffers are
+ * refused with DOPT_ERR_INVALID (use dopt_check_grads).  All calls on one GPU
+ * share the one array: calls that overlap in time on one GPU (e.g. on two
+ * streams) race and must not be issued; calls in stream order are safe.
+ *
+ * Arguments as dopt_check_grads.  Errors: DOPT_ERR_INVALID (null or
+ * misaligned pointers, buffer too large for the scratch), DOPT_ERR_RANGE (k),
+ * DOPT_ERR_HIP.
+ */
+int dopt_check_grads_noalloc(const dopt_layout *layout, int32_t k, const void *grad_buffer, double large_threshold,
+                             dopt_bucket_check *out, hipStream_t stream);
 
 /*
  * Sharded optimizer-state checkpoint in model-parameter space.  [DO] "三层继承

@@ -131,6 +131,7 @@ def _load():
         "dopt_reduce_prepare": ([VP, P(dopt_buffer_tensors), P(VP), I32, I32, ctypes.c_float, P(dopt_hparams), I32, D,
                                  VP, VP], ctypes.c_int),
         "dopt_check_grads": ([VP, I32, VP, D, VP, VP, VP], ctypes.c_int),
+        "dopt_check_grads_noalloc": ([VP, I32, VP, D, VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_apply": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
         "dopt_state_export": ([VP, P(dopt_buffer_tensors), VP, VP, VP, VP, VP], ctypes.c_int),
@@ -154,6 +155,7 @@ EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", 
             "dopt_layout_bucket", "dopt_layout_rank_window", "dopt_layout_param", "dopt_layout_group",
             "dopt_layout_state_numel", "dopt_workspace_bytes", "dopt_init_state", "dopt_step", "dopt_step_prepare", "dopt_step_stats",
             "dopt_step_finalize", "dopt_step_apply", "dopt_reduce_prepare", "dopt_check_grads",
+            "dopt_check_grads_noalloc",
             "dopt_state_export", "dopt_state_import", "dopt_state_scalars_get", "dopt_state_scalars_set",
             "dopt_stats_record_offset",
             "dopt_read_stats",
@@ -429,6 +431,20 @@ def dopt_check_grads(layout: Layout, k: int, grad_buffer, large_threshold: float
     g = _dev(grad_buffer, f"buffer {k} grad buffer", infos[k]["gd"], infos[k]["numel"])
     o = _dev(out, "bucket check output", None, 0, infos[k]["n_buckets"] * BUCKET_CHECK_BYTES)
     _check(_lib.dopt_check_grads(layout.handle, k, g, large_threshold, o, _ws(layout, workspace), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def dopt_check_grads_noalloc(layout: Layout, k: int, grad_buffer, large_threshold: float, out, stream=None):
+    """dopt_check_grads without a workspace: the library's static device
+    scratch holds the tables and partials (no allocation in the call)."""
+    infos = layout.infos()
+    if not 0 <= k < len(infos):
+        raise DoptError(-5, f"buffer index {k} out of range")
+    g = _dev(grad_buffer, f"buffer {k} grad buffer", infos[k]["gd"], infos[k]["numel"])
+    o = _dev(out, "bucket check output", None, 0, infos[k]["n_buckets"] * BUCKET_CHECK_BYTES)
+    _check(_lib.dopt_check_grads_noalloc(layout.handle, k, g, large_threshold, o, _stream(stream)))
 
 
 def bucket_checks(raw: bytes, n: int) -> List[Dict]:

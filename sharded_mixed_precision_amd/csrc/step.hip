@@ -21,6 +21,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -697,14 +698,37 @@ static_assert(sizeof(CheckPartial) == 16, "check partial size");
 
 constexpr int kCheckLoads = static_cast<int>(kCheckTile / kTile);
 
-template <int GD>
+// Bounds of check tile t from the bucket table alone: the last bucket whose
+// first check tile is at most t (a wave-uniform binary search), and the
+// tile's place in it.  Equal to the per-tile table the mapper builds.
+__device__ __forceinline__ void check_tile_bounds(const CheckBucket *__restrict__ bk, int32_t nb, int64_t t,
+                                                  int64_t &start, int64_t &end) {
+    int32_t lo = 0, hi = nb - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (bk[mid].tile_base <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    start = bk[lo].offset + (t - bk[lo].tile_base) * kCheckTile;
+    end = bk[lo].offset + bk[lo].numel;
+}
+
+// SEARCH: the tile bounds come from the bucket table (check_tile_bounds)
+// instead of the per-tile table ct.
+template <int GD, bool SEARCH>
 __global__ void __launch_bounds__(kBlock) k_check(const void *__restrict__ grad, const CheckTile *__restrict__ ct,
-                                                 int64_t n_tiles, CheckPartial *__restrict__ part) {
+                                                 const CheckBucket *__restrict__ bk, int32_t nb, int64_t n_tiles,
+                                                 CheckPartial *__restrict__ part) {
     __shared__ double s_acc[kBlock / 64];
     __shared__ float s_mx[kBlock / 64];
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        const int64_t base = ct[t].start;
-        const int64_t end = ct[t].end;
+        int64_t base, end;
+        if (SEARCH) {
+            check_tile_bounds(bk, nb, t, base, end);
+        } else {
+            base = ct[t].start;
+            end = ct[t].end;
+        }
         Raw8 raw[kCheckLoads];
         // Loads past the bucket end are clamped to its last 8 (16-bit) or 4
         // (fp32) elements (the bucket holds at least 128 elements from the
@@ -803,6 +827,19 @@ __global__ void __launch_bounds__(kBlock) k_check_finish(const CheckPartial *__r
         out[b].has_inf = isinf(sm) ? 1 : 0;
         out[b].large = (thr > 0.0 && static_cast<double>(sm) > thr) ? 1 : 0;
     }
+}
+
+// Up to kTableBatch bucket-table entries, passed by value (kernel arguments
+// hold up to 4 KB), written to dst by one wave.
+constexpr int kTableBatch = 160;
+struct TableBatch {
+    CheckBucket e[kTableBatch];
+    int32_t n;
+};
+static_assert(sizeof(TableBatch) <= 4000, "table batch must fit the kernel argument space");
+
+__global__ void __launch_bounds__(64) k_write_table(CheckBucket *__restrict__ dst, TableBatch tb) {
+    for (int i = threadIdx.x; i < tb.n; i += 64) dst[i] = tb.e[i];
 }
 
 // ---- pass 2: clip + AdamW + bias correction + write-back --------------------
@@ -1036,6 +1073,8 @@ static bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) % DO
 
 static char *ws_ptr(void *ws, int64_t off) { return static_cast<char *>(ws) + off; }
 
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
 static int check_bufs(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *ws, bool need_grad) {
     if (!L || !bufs || !ws) return fail(DOPT_ERR_INVALID, "null layout, tensors or workspace");
     if (!aligned(ws)) return fail(DOPT_ERR_INVALID, "workspace is not 256-byte aligned");
@@ -1224,6 +1263,58 @@ static int state_copy(const dopt_layout *L, const dopt_buffer_tensors *bufs, flo
     return DOPT_OK;
 }
 
+// Scan of one buffer's buckets: k_check over its check tiles, then
+// k_check_finish per bucket.  SEARCH: tile bounds from the bucket table.
+template <bool SEARCH>
+static int launch_check(const Buffer &B, const void *grad, const CheckTile *ct, const CheckBucket *bk, int32_t nb,
+                        CheckPartial *part, double thr, dopt_bucket_check *out, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(std::min<int64_t>(B.chk_tiles, kCheckMaxBlocks)));
+    if (B.gd == DOPT_BF16)
+        k_check<DOPT_BF16, SEARCH><<<grid, kBlock, 0, stream>>>(grad, ct, bk, nb, B.chk_tiles, part);
+    else if (B.gd == DOPT_F16)
+        k_check<DOPT_F16, SEARCH><<<grid, kBlock, 0, stream>>>(grad, ct, bk, nb, B.chk_tiles, part);
+    else
+        k_check<DOPT_F32, SEARCH><<<grid, kBlock, 0, stream>>>(grad, ct, bk, nb, B.chk_tiles, part);
+    int rc = check_launch("launch k_check");
+    if (rc) return rc;
+    k_check_finish<<<nb, kBlock, 0, stream>>>(part, bk, nb, B.chk_tiles, thr, out);
+    return check_launch("launch k_check_finish");
+}
+
+// ---- the allocation-free bucket check ------------------------------------------
+//
+// dopt_check_grads_noalloc keeps its bucket table and its per-check-tile
+// partials in `scratch`, a device array of fixed size that every GPU holds
+// from module load to process end.  On the host the array's name is only a
+// stand-in for the device symbol: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current, on the entry point's
+// first call there) and only that address is ever passed to a kernel.
+// Calls on one GPU share the array, so calls that overlap in time on one GPU
+// race; every call rewrites the table and every partial it reads.
+constexpr int64_t kNoAllocScratchBytes = DOPT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static char *g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_rc[kMaxDevices];
+
+static int scratch_on_current_device(char **out) {
+    int dev = -1;
+    int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (rc) return rc;
+    if (dev < 0 || dev >= kMaxDevices) return fail(DOPT_ERR_INVALID, "device index beyond the library's table");
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_rc[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    });
+    if (g_scratch_rc[dev] != hipSuccess)
+        return fail(DOPT_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(g_scratch_rc[dev]));
+    *out = g_scratch_ptr[dev];
+    return DOPT_OK;
+}
+
 }  // namespace dopt
 
 using namespace dopt;
@@ -1363,14 +1454,38 @@ int dopt_check_grads(const dopt_layout *L, int32_t k, const void *grad, double t
     const CheckTile *ct = reinterpret_cast<const CheckTile *>(ws_ptr(ws, B.ws_chk_tile));
     CheckPartial *part = reinterpret_cast<CheckPartial *>(ws_ptr(ws, B.ws_chk_part));
     const int32_t nb = static_cast<int32_t>(B.chk.size());
-    const dim3 grid(static_cast<uint32_t>(std::min<int64_t>(B.chk_tiles, kCheckMaxBlocks)));
-    if (B.gd == DOPT_BF16) k_check<DOPT_BF16><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
-    else if (B.gd == DOPT_F16) k_check<DOPT_F16><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
-    else k_check<DOPT_F32><<<grid, kBlock, 0, stream>>>(grad, ct, B.chk_tiles, part);
-    int rc = check_launch("launch k_check");
+    return launch_check<false>(B, grad, ct, bk, nb, part, thr, out, stream);
+}
+
+int dopt_check_grads_noalloc(const dopt_layout *L, int32_t k, const void *grad, double thr, dopt_bucket_check *out,
+                             hipStream_t stream) {
+    if (!L || !grad || !out) return fail(DOPT_ERR_INVALID, "null layout, grad buffer or output");
+    if (k < 0 || k >= static_cast<int32_t>(L->buffers.size())) return fail(DOPT_ERR_RANGE, "buffer index");
+    if (!aligned(grad) || reinterpret_cast<uintptr_t>(out) % 8 != 0)
+        return fail(DOPT_ERR_INVALID, "grad buffer not 256-byte aligned, or output not 8-byte aligned");
+    const Buffer &B = L->buffers[k];
+    const int64_t nb = static_cast<int64_t>(B.chk.size());
+    const int64_t tab = align256(nb * static_cast<int64_t>(sizeof(CheckBucket)));
+    const int64_t need = tab + B.chk_tiles * static_cast<int64_t>(sizeof(CheckPartial));
+    if (need > kNoAllocScratchBytes)
+        return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + " needs " + std::to_string(need) +
+                                          " bytes of scratch; the static scratch holds " +
+                                          std::to_string(kNoAllocScratchBytes) + " (use dopt_check_grads)");
+    char *base = nullptr;
+    int rc = scratch_on_current_device(&base);
     if (rc) return rc;
-    k_check_finish<<<nb, kBlock, 0, stream>>>(part, bk, nb, B.chk_tiles, thr, out);
-    return check_launch("launch k_check_finish");
+    CheckBucket *bk = reinterpret_cast<CheckBucket *>(base);
+    CheckPartial *part = reinterpret_cast<CheckPartial *>(base + tab);
+    // the bucket table goes into the scratch by kernel arguments (no host
+    // copy), kTableBatch entries per launch
+    for (int64_t b0 = 0; b0 < nb; b0 += kTableBatch) {
+        TableBatch tb;
+        tb.n = static_cast<int32_t>(std::min<int64_t>(kTableBatch, nb - b0));
+        std::memcpy(tb.e, B.chk.data() + b0, size_t(tb.n) * sizeof(CheckBucket));
+        k_write_table<<<1, 64, 0, stream>>>(bk + b0, tb);
+        if ((rc = check_launch("launch k_write_table"))) return rc;
+    }
+    return launch_check<true>(B, grad, nullptr, bk, static_cast<int32_t>(nb), part, thr, out, stream);
 }
 
 int dopt_state_export(const dopt_layout *L, const dopt_buffer_tensors *bufs, float *master, float *exp_avg,

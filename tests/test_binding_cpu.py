@@ -119,3 +119,13 @@ def test_reduce_chunks_and_exports(L):
     ok, short = torch.zeros(n), torch.zeros(n - 1)
     _err(lambda: D.dopt_state_export(L, t, 4096, short, ok, 0), "export exp_avg", "at least")
     _err(lambda: D.dopt_state_import(L, t, ok.double(), ok, ok, 0), "import master", "dtype")
+
+
+def test_noalloc_check_refuses_buffers_beyond_its_static_scratch():
+    # 2^34 elements: 2^20 check tiles of 16 B = 16 MiB of partials plus the
+    # bucket table, more than the library's static scratch holds.  The library
+    # refuses before any device work (the addresses are never used).
+    L = D.dopt_build_ranges([ParamSpec("huge", 1 << 34, "bf16", "bf16")], 1024, 0, 0)
+    _err(lambda: D.dopt_check_grads_noalloc(L, 0, 1 << 20, 1.0, 1 << 21), "scratch", "16777216")
+    assert D.NOALLOC_SCRATCH_BYTES == 16 << 20
+    _err(lambda: D.dopt_check_grads_noalloc(L, 1, 1 << 20, 1.0, 1 << 21), "out of range")
