@@ -110,6 +110,7 @@ def _load():
         "or_decide": ([P(Stats), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Scalars)], ctypes.c_int),
         "or_apply": ([VP, P(Arrays), P(Scalars)], None),
         "or_apply_elems": ([I32, I32, I64, VP, VP, VP, VP, VP, VP, P(Scalars)], None),
+        "or_apply_range": ([VP, I32, P(Arrays), P(Scalars), I64, I64], None),
         "or_step": ([VP, P(Arrays), P(Scaler), P(I64), P(HParams), I32, ctypes.c_double, P(Stats)], ctypes.c_int),
         "or_inv_scale": ([P(Scaler)], ctypes.c_float),
         "or_state_export": ([VP, P(Arrays), VP, VP, VP], I64),

@@ -702,6 +702,33 @@ void or_apply(const or_layout *L, or_arrays *bufs, const or_scalars *s) {
     }
 }
 
+/*
+ * S4 restricted to arena slots [lo, hi) of buffer k: the update of or_apply
+ * for the shard elements in that range.  Every element's update reads only
+ * its own grad, master, m and v and the step's scalars, so a caller may split
+ * one large pass into disjoint ranges (on threads) without changing any
+ * result.
+ */
+void or_apply_range(const or_layout *L, int32_t k, or_arrays *bufs, const or_scalars *s, int64_t lo, int64_t hi) {
+    if (s->skip) return;
+    const ob_buffer *B = &L->buf[k];
+    for (int64_t q = 0; q < B->n_segs; ++q) {
+        int32_t h = L->p[B->seg_param[q]].hgroup;
+        int64_t a = B->seg_start[q], e = B->seg_start[q] + B->seg_len[q];
+        if (a < lo) a = lo;
+        if (e > hi) e = hi;
+        for (int64_t i = a; i < e; ++i) {
+            float raw = load_f32(bufs[k].grad, B->gd, i);
+            if (B->pd == OR_F32) {
+                adamw_elem(raw, (float *)bufs[k].param + i, &bufs[k].m[i], &bufs[k].v[i], s, h);
+            } else {
+                adamw_elem(raw, &bufs[k].master[i], &bufs[k].m[i], &bufs[k].v[i], s, h);
+                store_param(bufs[k].param, B->pd, i, bufs[k].master[i]);
+            }
+        }
+    }
+}
+
 void or_apply_elems(int32_t param_dtype, int32_t grad_dtype, int64_t n, const int32_t *hgroup, const void *grad,
                     float *master, float *m, float *v, void *param_out, const or_scalars *s) {
     if (s->skip) return;

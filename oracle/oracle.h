@@ -151,6 +151,9 @@ int or_decide(or_stats *st, or_scaler *sc, int64_t *t, const or_hparams *hp, int
 /* S4: clip + AdamW + write-back over the rank's shard elements. */
 void or_apply(const or_layout *L, or_arrays *bufs, const or_scalars *s);
 /* S4 on a list of elements (each with its own hyper-group). */
+/* S4 restricted to arena slots [lo, hi) of buffer k (the same update per
+ * element as or_apply; disjoint ranges may run on different threads). */
+void or_apply_range(const or_layout *L, int32_t k, or_arrays *bufs, const or_scalars *s, int64_t lo, int64_t hi);
 void or_apply_elems(int32_t param_dtype, int32_t grad_dtype, int64_t n, const int32_t *hgroup,
                     const void *grad, float *master, float *m, float *v, void *param_out,
                     const or_scalars *s);

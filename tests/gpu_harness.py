@@ -311,6 +311,149 @@ def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[i
     return report
 
 
+# ------------------------------------------------- full parity, chunked ---
+
+def _valid_ranges(O: oracle.Layout, k: int):
+    s, ln, _ = O.segments(k)
+    return list(zip(s.tolist(), (s + ln).tolist()))
+
+
+def _gaps(ranges, n):
+    """Arena slots [lo, hi) between and after the shard segments."""
+    out, cur = [], 0
+    for a, b in ranges:
+        if a > cur:
+            out.append((cur, a))
+        cur = max(cur, b)
+    if cur < n:
+        out.append((cur, n))
+    return out
+
+
+def run_full_chunked(case: Case, workers: int = 16, chunk: int = 1 << 26) -> List[dict]:
+    """Every shard element compared after every step at full size, with the
+    oracle split into disjoint arena ranges run on host threads: the
+    statistics by or_grad_stats_range (partials added in range order), the
+    update by or_apply_range (each element's update depends on its own values
+    only), both pinned on the CPU to equal the whole-window calls.  The device
+    arrays are copied back range by range and compared with the oracle's."""
+    t0 = time.time()
+    lib = oracle.lib()
+    dev = DeviceRun(case)
+    O = oracle.Layout(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw, case.instances)
+    nb = O.num_buffers
+    infos = []
+    for k in range(nb):
+        b = O.buffer(k)
+        pd, gd = {0: "f32", 1: "bf16", 2: "f16"}[b["param_dtype"]], {0: "f32", 1: "bf16", 2: "f16"}[b["grad_dtype"]]
+        n = dev.L.buffer(k)["arena_numel"]
+        assert n == -(-max(b["window_numel"], 1) // 2048) * 2048
+        infos.append((pd, gd, n))
+    ranges = [_valid_ranges(O, k) for k in range(nb)]
+    host, params0, gap_bits = [], [], []
+    for k, (pd, gd, n) in enumerate(infos):
+        p = host_weights(case, k, pd, n)
+        params0.append(p)
+        pbits = to_bits(p)
+        gap_bits.append([(lo, hi, pbits[lo:hi].copy()) for lo, hi in _gaps(ranges[k], n)])
+        master = np.zeros(n, np.float32) if pd != "f32" else None
+        host.append({"param": pbits, "master": master, "m": np.zeros(n, np.float32), "v": np.zeros(n, np.float32),
+                     "grad": torch.empty(n, dtype=synth.torch_dtype(gd), pin_memory=torch.cuda.is_available())})
+    dev.init(params0)
+    jobs = [(k, lo, min(lo + chunk, infos[k][2])) for k in range(nb) for lo in range(0, infos[k][2], chunk)]
+
+    def init_master(job):
+        k, lo, hi = job
+        pd = infos[k][0]
+        h = host[k]
+        if pd == "bf16":
+            lib.or_bf16_to_f32_n(h["param"][lo:].ctypes.data, h["master"][lo:].ctypes.data, hi - lo)
+        elif pd == "f16":
+            lib.or_f16_to_f32_n(h["param"][lo:].ctypes.data, h["master"][lo:].ctypes.data, hi - lo)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(init_master, jobs))
+    arrays = (oracle.Arrays * nb)()
+    for k, h in enumerate(host):
+        arrays[k] = oracle.arrays(h["grad"], h["param"], h["master"], h["m"], h["v"])
+    log(f"[fullsize] {case.name}: init done {time.time() - t0:.1f}s, arenas {[i[2] for i in infos]}")
+    scaler = oracle.make_scaler(case.dynamic, case.initial_scale)
+    t = ctypes.c_int64(0)
+    hpa = oracle.make_hparams(case.hparams)
+    pos = inf_position(case, O) if case.inf_step else None
+    keys = [("master", "master"), ("exp_avg", "m"), ("exp_avg_sq", "v"), ("param", "param")]
+    report = []
+    for s in range(1, case.steps + 1):
+        ts = time.time()
+        for k, (pd, gd, n) in enumerate(infos):
+            host_grads(case, k, gd, n, s, out=host[k]["grad"])
+            if pos is not None and s == case.inf_step and pos[0] == k:
+                host[k]["grad"][pos[1]] = case.inf_value
+        tg = time.time()
+        st = oracle_stats_parallel(O, [h["grad"] for h in host], float(np.float32(1.0 / scaler.scale)), workers)
+        sc = oracle.Scalars()
+        assert lib.or_decide(ctypes.byref(st), ctypes.byref(scaler), ctypes.byref(t), hpa, len(case.hparams),
+                             case.max_norm, ctypes.byref(sc)) == 0
+
+        def apply(job):
+            k, lo, hi = job
+            lib.or_apply_range(O.handle, k, arrays, ctypes.byref(sc), lo, hi)
+
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(apply, jobs))
+        to = time.time()
+        got = dev.step([h["grad"] for h in host])
+        check_stats(got, st, s)
+
+        def compare(job):
+            """(elements compared, bit-identical, max param ulp) of one range;
+            raises on a value outside the tolerance."""
+            k, lo, hi = job
+            pd = infos[k][0]
+            out = []
+            for dkey, hkey in keys:
+                if hkey == "master" and pd == "f32":
+                    continue
+                d = to_bits(dev.A.bufs[k][dkey][lo:hi].cpu())
+                r = host[k][hkey][lo:hi]
+                valid = [(max(a, lo) - lo, min(b, hi) - lo) for a, b in ranges[k] if a < hi and b > lo]
+                cnt = sum(b - a for a, b in valid)
+                if np.array_equal(d.view(np.uint8), r.view(np.uint8)):
+                    out.append((hkey, cnt, cnt, 0))
+                    continue
+                m = np.zeros(hi - lo, bool)
+                for a, b in valid:
+                    m[a:b] = True
+                same = int(np.count_nonzero((d.view(np.uint8).reshape(hi - lo, -1) ==
+                                             r.view(np.uint8).reshape(hi - lo, -1)).all(axis=1) & m))
+                if hkey == "param" and pd != "f32":
+                    res = check_param(f"{case.name} s{s} {hkey}[{k}] [{lo},{hi})", d[m], r[m], pd)
+                    out.append((hkey, cnt, same, res["max_ulp"]))
+                else:
+                    check_f32(f"{case.name} s{s} {hkey}[{k}] [{lo},{hi})", d[m], r[m])
+                    out.append((hkey, cnt, same, 0))
+            return out
+
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            parts = [x for part in ex.map(compare, jobs) for x in part]
+        rep = {"step": s, "norm_dev": got["grad_norm"], "norm_ref": st.norm, "skipped": got["skipped"]}
+        for hkey in ("master", "m", "v", "param"):
+            sel = [p for p in parts if p[0] == hkey]
+            if sel:
+                n_el, n_same = sum(p[1] for p in sel), sum(p[2] for p in sel)
+                rep[hkey] = {"n": n_el, "bit_exact": n_same / max(n_el, 1), "max_ulp": max(p[3] for p in sel)}
+        for k, gaps in enumerate(gap_bits):  # slots that hold no param element are never written
+            pdev = dev.A.bufs[k]["param"]
+            for lo, hi, bits in gaps:
+                assert np.array_equal(to_bits(pdev[lo:hi].cpu()).view(np.uint8), bits.view(np.uint8)), \
+                    f"step {s}: param arena gap [{lo},{hi}) of buffer {k} written"
+        report.append(rep)
+        log(f"[fullsize] {case.name} step {s}: gen {tg - ts:.1f}s oracle {to - tg:.1f}s device+compare "
+            f"{time.time() - to:.1f}s; {rep}")
+    log(f"[fullsize] {case.name}: every element compared after each of {case.steps} steps in {time.time() - t0:.1f}s")
+    return report
+
+
 # --------------------------------------------------------- sampled parity ---
 
 def _pick_samples(O: oracle.Layout, k: int, n_rand: int, seed: int) -> np.ndarray:
@@ -324,16 +467,28 @@ def _pick_samples(O: oracle.Layout, k: int, n_rand: int, seed: int) -> np.ndarra
     q = np.searchsorted(c, j, side="right")
     before = np.where(q > 0, c[np.maximum(q - 1, 0)], 0)
     idx = s[q] + (j - before)
-    # every segment's first and last element, and the elements around each
-    # 2048-element tile boundary inside the first segments
-    edges = np.concatenate([s, s + ln - 1])
+    # every shard element of every boundary tile: the 2048-slot tiles that
+    # hold a segment's first or last element or a bucket window's first or
+    # last slot (the tiles the kernels take element by element)
+    ends = np.concatenate([s, s + ln - 1])
+    nbk = O.buffer(k)["n_buckets"]
+    wins = []
+    for b in range(nbk):
+        bk = O.bucket(k, b)
+        if bk["shard"] > 0:
+            wins += [bk["arena_offset"], bk["arena_offset"] + bk["shard"] - 1]
+    tiles = np.unique(np.concatenate([ends, np.array(wins, np.int64)]) // 2048)
     tb = []
-    for a, b in zip(s[:8].tolist(), (s + ln)[:8].tolist()):
-        t = (a // 2048 + 1) * 2048
-        while t < b and len(tb) < 256:
-            tb += [t - 1, t]
-            t += 2048 * 97
-    return np.unique(np.concatenate([idx, edges, np.array(tb, np.int64)]).astype(np.int64))
+    for tl in tiles.tolist():
+        lo, hi = tl * 2048, tl * 2048 + 2048
+        first = max(int(np.searchsorted(s + ln, lo, side="right")), 0)
+        for q in range(first, len(s)):
+            a, b = int(s[q]), int(s[q] + ln[q])
+            if a >= hi:
+                break
+            tb.append(np.arange(max(a, lo), min(b, hi), dtype=np.int64))
+    tb = np.concatenate(tb) if tb else np.zeros(0, np.int64)
+    return np.unique(np.concatenate([idx, ends, tb]).astype(np.int64))
 
 
 def oracle_stats_parallel(O: oracle.Layout, grads: List[torch.Tensor], inv_scale: float, workers: int = 16,

@@ -38,6 +38,21 @@ def test_gpt2_small_workload_full():
     assert rep[-1]["param0"]["n"] == 15_554_976
 
 
+def test_chunked_full_compare_on_gpt2_small_and_a_gapped_layout():
+    # the threaded full-size harness (used on request for the largest
+    # workloads) on small windows split into many ranges, one with
+    # alignment gaps, bucket padding and an overflow-skipped step
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.steps = 3
+    rep = H.run_full_chunked(case, chunk=1 << 20)
+    assert rep[-1]["master"]["n"] == 15_554_976 and rep[-1]["param"]["bit_exact"] == 1.0
+    params = [ParamSpec(f"p{i}", n, "bf16", "bf16") for i, n in enumerate([1000, 77, 4097, 3, 20000, 9, 131])]
+    case = H.Case("odd-chunked", params, 8, 5, bucket_size=2000, steps=4, dynamic=True, initial_scale=1024.0,
+                  inf_step=2)
+    rep = H.run_full_chunked(case, chunk=4096)
+    assert [r["skipped"] for r in rep] == [0, 1, 0, 0]
+
+
 @pytest.mark.timeout(600)
 def test_llama3_8b_workload_sampled():
     H.run_sampled(H.case_from_workload(synth.WORKLOADS["llama3-8b"]))
