@@ -1,7 +1,6 @@
-"""Build the native programs of tests/native: abi_step, a C++ consumer of
+"""Build the native program of tests/native: abi_step, a C++ consumer of
 libdopt.so (host code only: it calls the C ABI with hipMalloc'd buffers, no
-Python), and stream_roof, the HBM streaming roof measured with hand-written
-kernels (not linked to the library)."""
+Python)."""
 from __future__ import annotations
 
 import os
@@ -11,7 +10,6 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 EXE = os.path.join(HERE, "abi_step")
-ROOF = os.path.join(HERE, "stream_roof")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -32,9 +30,6 @@ def build(verbose: bool = False) -> str:
                    "-Wl,-rpath,$ORIGIN/../../sharded_mixed_precision_amd", "-o", EXE + ".tmp"],
          "tests/native/abi_step", verbose)
     os.replace(EXE + ".tmp", EXE)
-    _run(common + ["-O3", os.path.join(HERE, "stream_roof.hip"), "-o", ROOF + ".tmp"],
-         "tests/native/stream_roof", verbose)
-    os.replace(ROOF + ".tmp", ROOF)
     return EXE
 
 
