@@ -43,6 +43,7 @@ METRIC = "shard AdamW step: Gparams/s and achieved HBM GB/s (% of peak), 1 MI355
 ES = {"f32": 4, "bf16": 2, "f16": 2}
 APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
 SMALL_WINDOW = 64 << 20  # shard elements up to which the default step counts are large
+REGION_ELEMS = 1 << 27  # arena elements per placement region
 
 # HBM traffic of k_apply measured with rocprofv3 PMC counters (FETCH_SIZE,
 # WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
@@ -53,6 +54,9 @@ MEASURED_TRAFFIC = {
     "gpt2-small": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 436853012},
     # both buffers' pass-2 launches of one step (bf16 params with fp32 grads + fp32 norms)
     "llama3-8b": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 30176594637},
+    # FETCH_SIZE 46,269,124.20 KiB * 2.0 + WRITE_SIZE 92,128,333.61 KiB * 1.0, averaged over the 37
+    # dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
+    "dense-7b": {"src": "d6256e3464ba7df1", "bytes_per_launch": 189098579978},
 }
 
 
@@ -348,11 +352,16 @@ def main():
                          "dp_size received bf16 chunks + pass 1 (dopt_reduce_prepare); check: the whole-bucket "
                          "NaN/Inf/large scan of the rank's full local grad buffers (dopt_check_grads); checkpoint: the "
                          "model-space export and import of the rank's optimizer state (dopt_state_export / _import)")
+    ap.add_argument("--placement", choices=["auto", "regions", "sets"], default="auto",
+                    help="arena placement search: 'regions' backs each large buffer's arrays region by region "
+                         "(2^27 elements) and keeps, per region, the fastest of the candidate backings for pass 2; "
+                         "'sets' allocates whole candidate arena sets; auto: regions when a buffer spans at least "
+                         "4 regions, else sets")
     ap.add_argument("--placement-tries", type=int, default=8,
                     help="candidate arena placements tried at start-up, the fastest for pass 2 kept (1: plain "
                          "allocation); capped by free device memory")
     ap.add_argument("--flush-llc", action="store_true",
-                    help="step mode: write a 512 MiB buffer before each timed step, so that no step data is left in "
+                    help="step mode: read a 512 MiB buffer before each timed step, so that no step data is left in "
                          "the 256 MB last-level cache; each step is then timed on its own with HIP events and "
                          "ms_per_step is their mean")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -390,7 +399,7 @@ def main():
     if args.mode != "step":
         run_other_mode(args, w)
         return
-    res = measure_step(w, args.steps, args.warmup, args.placement_tries, args.flush_llc)
+    res = measure_step(w, args.steps, args.warmup, args.placement_tries, args.flush_llc, args.placement)
     out = {
         "metric": METRIC,
         "value": res["value"],
@@ -419,7 +428,7 @@ def main():
         import torch
         torch.cuda.empty_cache()
         sw = synth.WORKLOADS[args.secondary]
-        sec = measure_step(sw, None, None, args.placement_tries, False)
+        sec = measure_step(sw, None, None, args.placement_tries, False, args.placement)
         out["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "steps", "warmup", "hbm_GBps_step",
                                                  "hbm_frac_step", "roofline", "llc_flushed")}
         out["secondary"]["workload"] = sec["config"]["workload"]
@@ -445,7 +454,7 @@ def fill_device(t, sigma: float, seed: int, scale: float = 1.0, zero_frac: float
             part.masked_fill_(torch.rand(part.numel(), device=t.device, generator=g) < zero_frac, 0.0)
 
 
-def setup(w, placement_tries: int):
+def setup(w, placement_tries: int, placement: str = "auto"):
     """Layout, arenas (with the placement search) and seeded inputs of one
     workload, state initialised; returns (L, A, bufs_c, hp_c, sizes, alloc_seconds)."""
     import torch
@@ -455,8 +464,11 @@ def setup(w, placement_tries: int):
 
     params = synth.PARAM_LISTS[w.model]()
     L = D.dopt_build_ranges(params, w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
+    if placement == "auto":
+        big = max(L.buffer(k)["arena_numel"] for k in range(L.num_buffers))
+        placement = "regions" if big >= 4 * REGION_ELEMS else "sets"
     t_alloc = time.perf_counter()
-    A = DeviceArenas(L, placement_tries=placement_tries)
+    A = DeviceArenas(L, placement_tries=placement_tries, placement=placement, region_elems=REGION_ELEMS)
     torch.cuda.synchronize()
     t_alloc = time.perf_counter() - t_alloc
     sizes = {"E": 0, "bytes_step": 0, "apply_bytes": 0, "n_params": len(params)}
@@ -481,6 +493,17 @@ def placement_summary(A, seconds: float) -> dict:
     p = A.placement
     if p is None:
         return {"candidates": 1, "seconds": round(seconds, 3)}
+    if p.get("kind") == "regions":
+        out = {"kind": "regions", "seconds": round(seconds, 3), "buffers": []}
+        for b in p["buffers"]:
+            reg = b["last_sweep"]
+            out["buffers"].append({
+                "buffer": b["buffer"], "regions": b["regions"], "region_elems": b["region_elems"],
+                "sweeps": b["sweeps"], "region_ms_before_last_sweep": round(sum(r[1] for r in reg), 4),
+                "region_ms_kept": round(sum(r[2] for r in reg), 4),
+                "candidates_last_sweep": sum(r[3] for r in reg),
+                "fastest_region_ms": min(r[2] for r in reg), "slowest_region_ms": max(r[2] for r in reg[:-1] or reg)})
+        return out
     whole = p["pass2_ms"]
     out = {"whole_sets": {"n": len(whole), "kept_ms": whole[p["kept"]], "median_ms": round(statistics.median(whole), 4),
                           "worst_ms": max(whole), "all_ms": whole},
@@ -492,14 +515,14 @@ def placement_summary(A, seconds: float) -> dict:
     return out
 
 
-def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool) -> dict:
+def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placement: str = "auto") -> dict:
     """Time K back-to-back steps of one workload (or K steps each after an
     LLC flush), then pass 2 on its own, the flushed steps, and the skipped
     step for a dynamically scaled workload."""
     import torch
     import sharded_mixed_precision_amd as D
 
-    L, A, bufs_c, hp_c, sz, t_alloc = setup(w, placement_tries)
+    L, A, bufs_c, hp_c, sz, t_alloc = setup(w, placement_tries, placement)
     stream = torch.cuda.current_stream()
     E, bytes_step, apply_bytes = sz["E"], sz["bytes_step"], sz["apply_bytes"]
     progress(f"{w.name}: arenas placed in {t_alloc:.1f}s, inputs drawn, state initialised")
@@ -526,16 +549,21 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool) -> dic
     for _ in range(W):
         step()
     torch.cuda.synchronize()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
     torch.cuda.synchronize()
 
+    def evict():
+        """Read 512 MiB: the 256 MB last-level cache then holds none of the
+        step's data, only clean lines (a write would leave dirty lines whose
+        write-back the next step would pay for)."""
+        flush.sum()
+
     def flushed_steps():
-        """K steps, each timed on its own right after a 512 MiB write that
-        leaves no step data in the 256 MB last-level cache; total ms."""
+        """K steps, each timed on its own right after evict(); total ms."""
         ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         for i in range(K):
-            flush.fill_(i & 0xff)
+            evict()
             ev_s[i].record(stream)
             step()
             ev_e[i].record(stream)
@@ -558,7 +586,7 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool) -> dic
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for i in range(K):
         if flush_llc:
-            flush.fill_(i & 0xff)
+            evict()
         step_bracketed(ev_a[i], ev_b[i])
     torch.cuda.synchronize()
     apply_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / (K * APPLY_BATCH)
@@ -603,7 +631,7 @@ def run_other_mode(args, w):
     import torch
     import sharded_mixed_precision_amd as D
 
-    L, A, bufs_c, hp_c, sz, _ = setup(w, args.placement_tries)
+    L, A, bufs_c, hp_c, sz, _ = setup(w, args.placement_tries, args.placement)
     stream = torch.cuda.current_stream()
     if args.steps is None:
         args.steps = 50 if sz["E"] <= SMALL_WINDOW else 10

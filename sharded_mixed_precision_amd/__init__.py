@@ -141,6 +141,14 @@ def _load():
         "dopt_stats_record_offset": ([VP], I64),
         "dopt_read_stats": ([VP, VP, VP, P(dopt_stats)], ctypes.c_int),
         "dopt_last_error": ([], ctypes.c_char_p),
+        "dopt_vmm_granularity": ([I32, P(ctypes.c_size_t)], ctypes.c_int),
+        "dopt_vmm_reserve": ([ctypes.c_size_t, ctypes.c_size_t, P(ctypes.c_uint64)], ctypes.c_int),
+        "dopt_vmm_free": ([ctypes.c_uint64, ctypes.c_size_t], ctypes.c_int),
+        "dopt_vmm_create": ([I32, ctypes.c_size_t, P(ctypes.c_uint64)], ctypes.c_int),
+        "dopt_vmm_map": ([ctypes.c_uint64, ctypes.c_size_t, ctypes.c_uint64], ctypes.c_int),
+        "dopt_vmm_set_access": ([ctypes.c_uint64, ctypes.c_size_t, I32], ctypes.c_int),
+        "dopt_vmm_unmap": ([ctypes.c_uint64, ctypes.c_size_t], ctypes.c_int),
+        "dopt_vmm_release": ([ctypes.c_uint64], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -159,7 +167,9 @@ EXPORTED = ("dopt_build_ranges", "dopt_layout_free", "dopt_layout_num_buffers", 
             "dopt_state_export", "dopt_state_import", "dopt_state_scalars_get", "dopt_state_scalars_set",
             "dopt_stats_record_offset",
             "dopt_read_stats",
-            "dopt_last_error")
+            "dopt_last_error",
+            "dopt_vmm_granularity", "dopt_vmm_reserve", "dopt_vmm_free", "dopt_vmm_create", "dopt_vmm_map",
+            "dopt_vmm_set_access", "dopt_vmm_unmap", "dopt_vmm_release")
 
 
 def lib():
@@ -505,6 +515,46 @@ def dopt_state_scalars_set(layout: Layout, workspace, scalars: Dict, stream=None
 
 def dopt_last_error() -> str:
     return _lib.dopt_last_error().decode()
+
+
+# ---- device-memory placement helpers (include/dopt_vmm.h) ----
+
+def dopt_vmm_granularity(device: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.dopt_vmm_granularity(device, ctypes.byref(out)))
+    return out.value
+
+
+def dopt_vmm_reserve(nbytes: int, align: int = 0) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.dopt_vmm_reserve(nbytes, align, ctypes.byref(out)))
+    return out.value
+
+
+def dopt_vmm_free(va: int, nbytes: int):
+    _check(_lib.dopt_vmm_free(va, nbytes))
+
+
+def dopt_vmm_create(nbytes: int, device: int = 0) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.dopt_vmm_create(device, nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def dopt_vmm_map(va: int, nbytes: int, handle: int):
+    _check(_lib.dopt_vmm_map(va, nbytes, handle))
+
+
+def dopt_vmm_set_access(va: int, nbytes: int, device: int = 0):
+    _check(_lib.dopt_vmm_set_access(va, nbytes, device))
+
+
+def dopt_vmm_unmap(va: int, nbytes: int):
+    _check(_lib.dopt_vmm_unmap(va, nbytes))
+
+
+def dopt_vmm_release(handle: int):
+    _check(_lib.dopt_vmm_release(handle))
 
 
 hparams_array = _hparams

@@ -1,25 +1,36 @@
-"""Device memory for one rank's step, allocated with PyTorch.
+"""Device memory for one rank's step.
 
 Per flat buffer: the grad window arena (read by the step), the param window
 arena (written back), and the fp32 master / Adam m / Adam v arenas, all of
 ``arena_numel`` elements; plus the workspace.  Allocation only; the step runs
 in the library.
 
-Placement search.  On MI355X the speed of the step's second pass (half reads,
-half writes, five arrays streamed at once) depends on where the driver puts
-the arrays' pages in HBM: re-allocating the same arenas in one process moved
-that pass between 4.9 and 5.9 ms on the Llama-3-8B rank, with the same kernel.
-With ``placement_tries = n > 1`` the allocator creates up to n candidate sets
-of arenas, each while the earlier ones are still held (so each gets other
-pages), times the second pass on each (zeroed data, through the C ABI), keeps
-the fastest and frees the rest.  The number of whole sets is capped by the
-free device memory.  The kept set is then refined one array at a time: up to
-n candidates for that array, the others fixed, the fastest kept.  (Whole sets
-found the fast placements of the 16 GB Llama-3 ranks, which refining array by
-array alone did not; refining the best whole set took their step a further
-0.5-1% faster, and the 108 GB dense-7B state, of which only two sets fit,
-from 34.4 to 31.2 ms.)  The search runs once, before any data is loaded; the
-arenas then serve every step of the run.
+Placement.  The step's second pass reads four arrays and writes four at the
+same index at once, and on MI355X how fast it runs depends on where the
+arrays' physical pages sit relative to each other: the same kernel took
+4.9-5.9 ms on the Llama-3-8B rank from one allocation to the next.  Plain
+streams on the same arrays show that the placement decides the writes: five
+arrays written at once ran at 5.5 TB/s on an ordinary allocation and 7.2 TB/s
+on a fast one, while five read at once stayed near 6 TB/s on both; pass 2 ran
+at 5.1 and 6.1 TB/s.  Which pages are fast cannot be read from user space, so
+it is measured:
+
+- ``placement="regions"`` (large buffers): each array is a reserved address
+  range backed region by region (``dopt_vmm.h``; regions of 2^27 elements).
+  For every region and array, candidate backings are mapped in turn and
+  pass 2 is timed on that region alone; the fastest is kept.  Per region the
+  times fall into two groups (about 5.4 and 6.1 TB/s); two sweeps bring every
+  region to the faster one.  The search needs one spare region of memory and
+  took 0.7-5 s for the Llama-3 ranks and the 108 GB dense-7B state.
+- ``placement="sets"``: up to n whole candidate sets of arenas, each allocated
+  while the earlier ones are held, the fastest for pass 2 kept, then refined
+  one array at a time.  It finds the same 6.1 TB/s plateau when a fast set
+  turns up, but needs room for several copies of the state (two for
+  dense-7B) and took 18-20 s there.
+
+Either search runs once, before any data is loaded; the arenas then serve
+every step.  Without a search (the default) the arrays are plain PyTorch
+allocations.
 """
 from __future__ import annotations
 
@@ -33,9 +44,98 @@ TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float
 ES = {"f32": 4, "bf16": 2, "f16": 2}
 
 
+KEYS = ("grad", "param", "master", "exp_avg", "exp_avg_sq")
+# __cuda_array_interface__ type strings; bf16 has none and is viewed from int16
+_TYPESTR = {"f32": ("<f4", None), "f16": ("<f2", None), "bf16": ("<i2", torch.bfloat16)}
+
+
+class _Backing:
+    """A reserved device address range whose regions are backed by physical
+    allocations of their own (dopt_vmm.h).  Unmapped and released when the
+    last tensor viewing it goes away (the tensors hold a reference)."""
+
+    def __init__(self, nbytes: int, region_bytes: int, gran: int):
+        from . import dopt_vmm_create, dopt_vmm_map, dopt_vmm_reserve, dopt_vmm_set_access
+        # whole regions only (the tail of the last one is backed but unused):
+        # the access call on a remapped region was refused on MI355X for a
+        # region shorter than the others
+        region_bytes = -(-region_bytes // gran) * gran
+        self.nbytes = -(-nbytes // region_bytes) * region_bytes
+        self.region_bytes = region_bytes
+        self.va = dopt_vmm_reserve(self.nbytes, gran)
+        self.handles: List[int] = []
+        self.mapped = 0
+        try:
+            for off in range(0, self.nbytes, region_bytes):
+                size = min(region_bytes, self.nbytes - off)
+                h = dopt_vmm_create(size)
+                self.handles.append(h)
+                dopt_vmm_map(self.va + off, size, h)
+                self.mapped += 1
+            dopt_vmm_set_access(self.va, self.nbytes)
+        except Exception:
+            self.close()
+            raise
+
+    def region(self, j: int) -> Tuple[int, int]:
+        off = j * self.region_bytes
+        return self.va + off, min(self.region_bytes, self.nbytes - off)
+
+    def replace(self, j: int, h: int):
+        """Back region j with h (the caller keeps the old handle)."""
+        from . import DoptError, dopt_vmm_map, dopt_vmm_set_access, dopt_vmm_unmap
+        torch.cuda.synchronize()
+        va, size = self.region(j)
+        dopt_vmm_unmap(va, size)
+        dopt_vmm_map(va, size, h)
+        try:
+            dopt_vmm_set_access(va, size)
+        except DoptError:
+            dopt_vmm_set_access(self.va, self.nbytes)
+        self.handles[j] = h
+
+    def close(self):
+        from . import dopt_vmm_free, dopt_vmm_release, dopt_vmm_unmap
+        if getattr(self, "va", None) is None:
+            return
+        torch.cuda.synchronize()
+        for j in range(self.mapped):
+            va, size = self.region(j)
+            dopt_vmm_unmap(va, size)
+        for h in self.handles:
+            dopt_vmm_release(h)
+        dopt_vmm_free(self.va, self.nbytes)
+        self.va = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class _View:
+    def __init__(self, backing: _Backing, n: int, typestr: str):
+        self.backing = backing  # kept alive by every tensor made from this view
+        self.__cuda_array_interface__ = {"shape": (n,), "typestr": typestr, "data": (backing.va, False),
+                                         "version": 3, "strides": None}
+
+
+def _tensor_over(backing: _Backing, n: int, dt: str) -> torch.Tensor:
+    ts, view_as = _TYPESTR[dt]
+    t = torch.as_tensor(_View(backing, n, ts), device="cuda")
+    return t.view(view_as) if view_as is not None else t
+
+
 class DeviceArenas:
+    """placement "sets": up to placement_tries whole arena sets, then array by
+    array (below); "regions": the large buffers' arrays backed region by
+    region through dopt_vmm.h, each region's backing chosen by timing pass 2
+    on that region (region_search)."""
+
     def __init__(self, layout: Layout, device: str = "cuda", placement_tries: int = 1,
-                 timed_launches: int = 5):
+                 timed_launches: int = 5, placement: str = "sets", region_elems: int = 1 << 27,
+                 region_sweeps: int = 2):
         self.layout = layout
         self.device = device
         self.info = []
@@ -44,22 +144,26 @@ class DeviceArenas:
             pd, gd = DTYPE_NAMES[b["param_dtype"]], DTYPE_NAMES[b["grad_dtype"]]
             self.info.append({"pd": pd, "gd": gd, "n": b["arena_numel"], **b})
         self.placement: Optional[Dict] = None
-        if placement_tries > 1:
+        if placement == "regions":
+            self.bufs, self.workspace = self._region_search(placement_tries, timed_launches, region_elems,
+                                                            region_sweeps)
+        elif placement_tries > 1:
             self.bufs, self.workspace = self._search(placement_tries, timed_launches)
         else:
             self.bufs, self.workspace = self._alloc()
 
+    def _alloc_buffer(self, inf) -> Dict[str, torch.Tensor]:
+        n, pd, gd = inf["n"], inf["pd"], inf["gd"]
+        return {
+            "grad": torch.zeros(n, dtype=TORCH_DTYPES[gd], device=self.device),
+            "param": torch.zeros(n, dtype=TORCH_DTYPES[pd], device=self.device),
+            "master": torch.zeros(n, dtype=torch.float32, device=self.device) if pd != "f32" else None,
+            "exp_avg": torch.zeros(n, dtype=torch.float32, device=self.device),
+            "exp_avg_sq": torch.zeros(n, dtype=torch.float32, device=self.device),
+        }
+
     def _alloc(self) -> Tuple[List[Dict[str, torch.Tensor]], torch.Tensor]:
-        bufs = []
-        for inf in self.info:
-            n, pd, gd = inf["n"], inf["pd"], inf["gd"]
-            bufs.append({
-                "grad": torch.zeros(n, dtype=TORCH_DTYPES[gd], device=self.device),
-                "param": torch.zeros(n, dtype=TORCH_DTYPES[pd], device=self.device),
-                "master": torch.zeros(n, dtype=torch.float32, device=self.device) if pd != "f32" else None,
-                "exp_avg": torch.zeros(n, dtype=torch.float32, device=self.device),
-                "exp_avg_sq": torch.zeros(n, dtype=torch.float32, device=self.device),
-            })
+        bufs = [self._alloc_buffer(inf) for inf in self.info]
         ws = torch.zeros(self.layout.workspace_bytes, dtype=torch.uint8, device=self.device)
         return bufs, ws
 
@@ -148,6 +252,114 @@ class DeviceArenas:
                 torch.cuda.synchronize()
                 torch.cuda.empty_cache()
         return steps
+
+    def _region_search(self, tries: int, launches: int, region_elems: int, sweeps: int):
+        """Buffers of at least 4 regions get their five arrays (four for fp32
+        params) as reserved address ranges backed region by region; for every
+        region and array, up to `tries` candidate backings are mapped in turn
+        and pass 2 is timed on that region alone (a region-sized layout over
+        the same memory, through the C ABI); the fastest is kept.  Rejected
+        candidates are held until the region is done, so that each try gets
+        other physical memory.  A region whose time per element is within 1%
+        of the best region seen so far is not searched further.  Smaller
+        buffers get plain allocations."""
+        from . import (DoptError, dopt_build_ranges, dopt_init_state, dopt_step_apply, dopt_step_prepare,
+                       dopt_vmm_create, dopt_vmm_granularity, dopt_vmm_release, hparams_array, scaler_cfg)
+        gran = dopt_vmm_granularity(0)
+        bufs = [self._alloc_buffer(inf) if inf["n"] < 4 * region_elems else {} for inf in self.info]
+        ws = torch.zeros(self.layout.workspace_bytes, dtype=torch.uint8, device=self.device)
+        stream = torch.cuda.current_stream()
+        hp = hparams_array([(1e-3, 0.9, 0.999, 1e-8, 0.0)] * DOPT_MAX_HGROUPS)
+        report = []
+        self._backings = []
+        for k, inf in enumerate(self.info):
+            n = inf["n"]
+            if n < 4 * region_elems:
+                continue
+            keys = [key for key in KEYS if not (key == "master" and inf["pd"] == "f32")]
+            es = {"grad": ES[inf["gd"]], "param": ES[inf["pd"]], "master": 4, "exp_avg": 4, "exp_avg_sq": 4}
+            dts = {"grad": inf["gd"], "param": inf["pd"], "master": "f32", "exp_avg": "f32", "exp_avg_sq": "f32"}
+            back = {}
+            bufs[k] = {key: None for key in KEYS}
+            for key in keys:
+                back[key] = _Backing(n * es[key], region_elems * es[key], gran)
+                bufs[k][key] = _tensor_over(back[key], n, dts[key])
+                bufs[k][key].zero_()
+            self._backings.append(back)
+            nreg = -(-n // region_elems)
+            layouts = {}
+
+            class _P:
+                def __init__(self, numel):
+                    self.numel, self.param_dtype, self.grad_dtype = numel, inf["pd"], inf["gd"]
+
+            def region_ms(j):
+                lo = j * region_elems
+                m = min(region_elems, n - lo)
+                if m not in layouts:
+                    Lr = dopt_build_ranges([_P(m)], 1, 0, 0)
+                    layouts[m] = (Lr, torch.zeros(Lr.workspace_bytes, dtype=torch.uint8, device=self.device))
+                Lr, wsr = layouts[m]
+                rb = [{key: back[key].va + lo * es[key] for key in keys}]
+                if inf["pd"] == "f32":
+                    rb[0]["master"] = None
+                dopt_init_state(Lr, rb, scaler_cfg(False, 1.0), wsr, stream)
+                dopt_step_prepare(Lr, rb, hp, 0.0, wsr, stream)
+                dopt_step_apply(Lr, rb, wsr, stream)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(launches):
+                    dopt_step_apply(Lr, rb, wsr, stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / launches, m
+
+            best_rate = float("inf")  # ms per element of the fastest region so far
+            regions = []
+            for sweep in range(sweeps):
+                for j in range(nreg):
+                    first, m = region_ms(j)
+                    best = first
+                    tried = 0
+                    for key in keys:
+                        if best / m <= 1.01 * best_rate:
+                            break
+                        held = []
+                        for _ in range(tries):
+                            try:
+                                h = dopt_vmm_create(back[key].region(j)[1])
+                            except DoptError:
+                                break  # out of device memory for candidates
+                            old = back[key].handles[j]
+                            back[key].replace(j, h)
+                            lo = j * region_elems
+                            bufs[k][key][lo:lo + m].zero_()
+                            ms, _ = region_ms(j)
+                            tried += 1
+                            if ms < best:
+                                best = ms
+                                held.append(old)
+                            else:
+                                back[key].replace(j, old)
+                                held.append(h)
+                            if best / m <= 1.01 * best_rate:
+                                break
+                        torch.cuda.synchronize()
+                        for h in held:
+                            dopt_vmm_release(h)
+                    best_rate = min(best_rate, best / m)
+                    if sweep == sweeps - 1:  # [region, ms before, ms after, candidates tried]
+                        regions.append([j, round(first, 4), round(best, 4), tried])
+            report.append({"buffer": k, "regions": nreg, "region_elems": region_elems, "sweeps": sweeps,
+                           "last_sweep": regions})
+        for b in bufs:
+            for v in b.values():
+                if v is not None:
+                    v.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        self.placement = {"kind": "regions", "buffers": report}
+        return bufs, ws
 
     def state_bytes(self) -> int:
         tot = 0

@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libdopt.so")
-SOURCES = [os.path.join(HERE, "csrc", "mapper.cpp"), os.path.join(HERE, "csrc", "step.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "mapper.cpp"), os.path.join(HERE, "csrc", "step.hip"),
+           os.path.join(HERE, "csrc", "vmm.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

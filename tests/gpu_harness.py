@@ -66,6 +66,8 @@ class Case:
     reduce_scale: float = 1.0
     reduce_split: bool = False
     placement_tries: int = 1  # DeviceArenas placement search (1: plain allocation)
+    placement: str = "sets"  # "regions": large buffers backed region by region (dopt_vmm.h)
+    region_elems: int = 1 << 27
 
     def scale_at(self, step: int) -> float:
         if not self.dynamic:
@@ -191,7 +193,8 @@ class DeviceRun:
         self.D = D
         self.L = D.dopt_build_ranges(case.params, case.dp_size, case.dp_rank, case.bucket_size, case.busbw,
                                      case.instances)
-        self.A = DeviceArenas(self.L, placement_tries=case.placement_tries)
+        self.A = DeviceArenas(self.L, placement_tries=case.placement_tries, placement=case.placement,
+                              region_elems=case.region_elems)
         self.stream = torch.cuda.current_stream()
         self.case = case
 

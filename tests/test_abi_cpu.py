@@ -2,6 +2,7 @@
 declares, and its host range mapper is bit-exact against the oracle on the
 five workloads and on random layouts.  No device call is made here."""
 import ctypes
+import glob
 import os
 import random
 import re
@@ -23,9 +24,11 @@ def _dopt():
 
 def test_library_exports_every_declared_symbol():
     d = _dopt()
-    header = open(os.path.join(ROOT, "include", "dopt.h")).read()
-    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(dopt_\w+)\s*\(", header, re.M))
-    assert len(declared) >= 18
+    declared = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        header = open(h).read()
+        declared |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(dopt_\w+)\s*\(", header, re.M))
+    assert len(declared) >= 25 and "dopt_vmm_map" in declared and "dopt_check_grads_noalloc" in declared
     lib = ctypes.CDLL(d.LIB_PATH)
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} not exported"

@@ -58,3 +58,15 @@ def test_default_workload_is_the_largest_one_gpu_workload():
     assert ap_default and '"dense-7b"' in ap_default[0]
     w = synth.WORKLOADS["dense-7b"]
     assert w.dp_size == 1  # the whole model's state on one GPU
+
+
+def test_placement_summary_of_region_search():
+    class A:
+        placement = {"kind": "regions", "buffers": [
+            {"buffer": 0, "regions": 3, "region_elems": 1 << 27, "sweeps": 2,
+             "last_sweep": [[0, 0.70, 0.61, 5], [1, 0.62, 0.61, 0], [2, 0.20, 0.19, 2]]}]}
+    out = bench.placement_summary(A, 5.0)
+    b = out["buffers"][0]
+    assert out["kind"] == "regions" and b["regions"] == 3 and b["region_ms_kept"] == 1.41
+    assert b["region_ms_before_last_sweep"] == 1.52 and b["candidates_last_sweep"] == 7
+    assert b["fastest_region_ms"] == 0.19 and b["slowest_region_ms"] == 0.61

@@ -203,6 +203,26 @@ def test_placement_search_arenas():
     H.run_full(case)
 
 
+def test_region_placed_arenas():
+    """Arenas whose large arrays are reserved address ranges backed region by
+    region (dopt_vmm.h), each region's backing chosen by timing pass 2 on it:
+    the step over them equals the oracle element by element, and the arena
+    tensors are views of the reserved ranges.  Regions of 2^20 elements give
+    the GPT-2-small rank's arrays 15 regions each (the last one partly used)."""
+    case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
+    case.name, case.steps, case.placement_tries = "gpt2-regions", 3, 3
+    case.placement, case.region_elems = "regions", 1 << 20
+    dev = H.DeviceRun(case)
+    p = dev.A.placement
+    assert p["kind"] == "regions" and p["buffers"][0]["regions"] == 15
+    assert len(p["buffers"][0]["last_sweep"]) == 15
+    back = dev.A._backings[0]
+    assert dev.A.bufs[0]["master"].data_ptr() == back["master"].va
+    assert dev.A.bufs[0]["param"].dtype == torch.bfloat16 and dev.A.bufs[0]["param"].data_ptr() == back["param"].va
+    del dev, back
+    H.run_full(case)
+
+
 def test_deterministic():
     case = H.case_from_workload(synth.WORKLOADS["gpt2-small"])
     case.steps = 2
