@@ -51,9 +51,9 @@ REGION_ELEMS = 1 << 27  # arena elements per placement region
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    "gpt2-small": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 436853012},
-    # both buffers' pass-2 launches of one step (bf16 params with fp32 grads + fp32 norms)
-    "llama3-8b": {"src": "dc1dd6f10ef299f3", "bytes_per_launch": 30176594637},
+    # FETCH_SIZE 106,561.86 KiB * 2.0 + WRITE_SIZE 213,557.77 KiB * 1.0, averaged over 379 dispatches
+    # (profiles/k_apply_gpt2-small_kernel_trace.md)
+    "gpt2-small": {"src": "d6256e3464ba7df1", "bytes_per_launch": 436921853},
     # FETCH_SIZE 46,269,124.20 KiB * 2.0 + WRITE_SIZE 92,128,333.61 KiB * 1.0, averaged over the 37
     # dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
     "dense-7b": {"src": "d6256e3464ba7df1", "bytes_per_launch": 189098579978},
