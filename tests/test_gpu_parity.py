@@ -60,7 +60,10 @@ def test_llama3_8b_workload_sampled():
 
 @pytest.mark.timeout(900)
 def test_dense_7b_workload_sampled():
-    rep = H.run_sampled(H.case_from_workload(synth.WORKLOADS["dense-7b"]))
+    # on arenas placed region by region, as the bench runs this workload
+    case = H.case_from_workload(synth.WORKLOADS["dense-7b"])
+    case.placement, case.placement_tries = "regions", 2
+    rep = H.run_sampled(case)
     assert [r["skipped"] for r in rep] == [0, 0, 1, 0, 0]
 
 
