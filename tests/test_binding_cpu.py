@@ -129,3 +129,19 @@ def test_noalloc_check_refuses_buffers_beyond_its_static_scratch():
     _err(lambda: D.dopt_check_grads_noalloc(L, 0, 1 << 20, 1.0, 1 << 21), "scratch", "16777216")
     assert D.NOALLOC_SCRATCH_BYTES == 16 << 20
     _err(lambda: D.dopt_check_grads_noalloc(L, 1, 1 << 20, 1.0, 1 << 21), "out of range")
+
+
+def test_vmm_wrappers_report_hip_errors_as_dopt_errors():
+    # the placement helpers of dopt_vmm.h return the library's error codes; a
+    # bad handle or an empty size is refused before HIP is reached, and on a
+    # machine without a GPU the HIP calls themselves fail cleanly
+    with pytest.raises(D.DoptError) as e:
+        D.dopt_vmm_reserve(0)
+    assert e.value.code == -1 and "zero size" in str(e.value)
+    with pytest.raises(D.DoptError) as e:
+        D.dopt_vmm_create(0)
+    assert e.value.code == -1
+    if not torch.cuda.is_available():
+        with pytest.raises(D.DoptError) as e:
+            D.dopt_vmm_granularity(0)
+        assert e.value.code == -4 and "hipMemGetAllocationGranularity" in str(e.value)
