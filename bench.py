@@ -357,7 +357,12 @@ def main():
                          "(2^27 elements) and keeps, per region, the fastest of the candidate backings for pass 2; "
                          "'sets' allocates whole candidate arena sets; auto: regions when a buffer spans at least "
                          "4 regions, else sets")
-    ap.add_argument("--placement-tries", type=int, default=8,
+    # A one-time search of about 40-50 s for the 108 GB dense-7B state: against 2 sweeps, 1% and 8 candidates
+    # (6-7 s) it took that workload's pass 2 from 30.82-30.84 to 30.66-30.67 ms, two runs each on one box.
+    ap.add_argument("--region-sweeps", type=int, default=3, help="region search: passes over the regions")
+    ap.add_argument("--region-tolerance", type=float, default=0.003,
+                    help="region search: a region within this fraction of the fastest region rate seen is kept")
+    ap.add_argument("--placement-tries", type=int, default=12,
                     help="candidate arena placements tried at start-up, the fastest for pass 2 kept (1: plain "
                          "allocation); capped by free device memory")
     ap.add_argument("--flush-llc", action="store_true",
@@ -399,7 +404,8 @@ def main():
     if args.mode != "step":
         run_other_mode(args, w)
         return
-    res = measure_step(w, args.steps, args.warmup, args.placement_tries, args.flush_llc, args.placement)
+    res = measure_step(w, args.steps, args.warmup, args.placement_tries, args.flush_llc, args.placement,
+                       (args.region_sweeps, args.region_tolerance))
     out = {
         "metric": METRIC,
         "value": res["value"],
@@ -454,7 +460,7 @@ def fill_device(t, sigma: float, seed: int, scale: float = 1.0, zero_frac: float
             part.masked_fill_(torch.rand(part.numel(), device=t.device, generator=g) < zero_frac, 0.0)
 
 
-def setup(w, placement_tries: int, placement: str = "auto"):
+def setup(w, placement_tries: int, placement: str = "auto", region=(2, 0.01)):
     """Layout, arenas (with the placement search) and seeded inputs of one
     workload, state initialised; returns (L, A, bufs_c, hp_c, sizes, alloc_seconds)."""
     import torch
@@ -468,7 +474,8 @@ def setup(w, placement_tries: int, placement: str = "auto"):
         big = max(L.buffer(k)["arena_numel"] for k in range(L.num_buffers))
         placement = "regions" if big >= 4 * REGION_ELEMS else "sets"
     t_alloc = time.perf_counter()
-    A = DeviceArenas(L, placement_tries=placement_tries, placement=placement, region_elems=REGION_ELEMS)
+    A = DeviceArenas(L, placement_tries=placement_tries, placement=placement, region_elems=REGION_ELEMS,
+                     region_sweeps=region[0], region_tolerance=region[1])
     torch.cuda.synchronize()
     t_alloc = time.perf_counter() - t_alloc
     sizes = {"E": 0, "bytes_step": 0, "apply_bytes": 0, "n_params": len(params)}
@@ -515,14 +522,15 @@ def placement_summary(A, seconds: float) -> dict:
     return out
 
 
-def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placement: str = "auto") -> dict:
+def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placement: str = "auto",
+                 region=(2, 0.01)) -> dict:
     """Time K back-to-back steps of one workload (or K steps each after an
     LLC flush), then pass 2 on its own, the flushed steps, and the skipped
     step for a dynamically scaled workload."""
     import torch
     import sharded_mixed_precision_amd as D
 
-    L, A, bufs_c, hp_c, sz, t_alloc = setup(w, placement_tries, placement)
+    L, A, bufs_c, hp_c, sz, t_alloc = setup(w, placement_tries, placement, region)
     stream = torch.cuda.current_stream()
     E, bytes_step, apply_bytes = sz["E"], sz["bytes_step"], sz["apply_bytes"]
     progress(f"{w.name}: arenas placed in {t_alloc:.1f}s, inputs drawn, state initialised")

@@ -20,8 +20,10 @@ it is measured:
   For every region and array, candidate backings are mapped in turn and
   pass 2 is timed on that region alone; the fastest is kept.  Per region the
   times fall into two groups (about 5.4 and 6.1 TB/s); two sweeps bring every
-  region to the faster one.  The search needs one spare region of memory and
-  took 0.7-5 s for the Llama-3 ranks and the 108 GB dense-7B state.
+  region to the faster one.  The search holds at most one region of memory per
+  candidate and took 0.3-9 s for the Llama-3 ranks and the 108 GB dense-7B
+  state with 2 sweeps, 8 candidates and a 1% tolerance (40-50 s for dense-7B
+  with 3 sweeps, 12 candidates and 0.3%, which gained another 0.5%).
 - ``placement="sets"``: up to n whole candidate sets of arenas, each allocated
   while the earlier ones are held, the fastest for pass 2 kept, then refined
   one array at a time.  It finds the same 6.1 TB/s plateau when a fast set
@@ -135,7 +137,7 @@ class DeviceArenas:
 
     def __init__(self, layout: Layout, device: str = "cuda", placement_tries: int = 1,
                  timed_launches: int = 5, placement: str = "sets", region_elems: int = 1 << 27,
-                 region_sweeps: int = 2):
+                 region_sweeps: int = 2, region_tolerance: float = 0.01):
         self.layout = layout
         self.device = device
         self.info = []
@@ -146,7 +148,7 @@ class DeviceArenas:
         self.placement: Optional[Dict] = None
         if placement == "regions":
             self.bufs, self.workspace = self._region_search(placement_tries, timed_launches, region_elems,
-                                                            region_sweeps)
+                                                            region_sweeps, region_tolerance)
         elif placement_tries > 1:
             self.bufs, self.workspace = self._search(placement_tries, timed_launches)
         else:
@@ -253,15 +255,15 @@ class DeviceArenas:
                 torch.cuda.empty_cache()
         return steps
 
-    def _region_search(self, tries: int, launches: int, region_elems: int, sweeps: int):
+    def _region_search(self, tries: int, launches: int, region_elems: int, sweeps: int, tol: float = 0.01):
         """Buffers of at least 4 regions get their five arrays (four for fp32
         params) as reserved address ranges backed region by region; for every
         region and array, up to `tries` candidate backings are mapped in turn
         and pass 2 is timed on that region alone (a region-sized layout over
         the same memory, through the C ABI); the fastest is kept.  Rejected
         candidates are held until the region is done, so that each try gets
-        other physical memory.  A region whose time per element is within 1%
-        of the best region seen so far is not searched further.  Smaller
+        other physical memory.  A region whose time per element is within
+        `tol` (1%) of the best region seen so far is not searched further.  Smaller
         buffers get plain allocations."""
         from . import (DoptError, dopt_build_ranges, dopt_init_state, dopt_step_apply, dopt_step_prepare,
                        dopt_vmm_create, dopt_vmm_granularity, dopt_vmm_release, hparams_array, scaler_cfg)
@@ -322,7 +324,7 @@ class DeviceArenas:
                     best = first
                     tried = 0
                     for key in keys:
-                        if best / m <= 1.01 * best_rate:
+                        if best / m <= (1.0 + tol) * best_rate:
                             break
                         held = []
                         for _ in range(tries):
@@ -342,7 +344,7 @@ class DeviceArenas:
                             else:
                                 back[key].replace(j, old)
                                 held.append(h)
-                            if best / m <= 1.01 * best_rate:
+                            if best / m <= (1.0 + tol) * best_rate:
                                 break
                         torch.cuda.synchronize()
                         for h in held:
