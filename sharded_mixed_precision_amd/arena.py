@@ -129,6 +129,125 @@ def _tensor_over(backing: _Backing, n: int, dt: str) -> torch.Tensor:
     return t.view(view_as) if view_as is not None else t
 
 
+def search_regions(ops, nreg: int, keys, tries: int, sweeps: int, tol: float) -> List:
+    """The region search's policy, on an `ops` object that backs and times
+    regions: ops.region_ms(j) -> (ms, elements) times pass 2 on region j;
+    ops.create(key, j) -> a new backing for that region of that array (or
+    None when memory runs out); ops.current(key, j); ops.use(key, j, h) maps h
+    there; ops.release(h) frees a backing that is not mapped.
+
+    For every region, up to `tries` candidates per array are mapped in turn
+    and timed; the fastest backing is kept.  Rejected and replaced backings
+    are held until the array's candidates are done (so that each try gets
+    other memory) and then released.  A region whose time per element is
+    within `tol` of the best region rate seen so far is not searched further.
+    Returns, for the last sweep, [region, ms before, ms after, candidates
+    tried] per region."""
+    best_rate = None  # ms per element of the fastest region so far
+
+    def near_best(ms, m):
+        return best_rate is not None and ms / m <= (1.0 + tol) * best_rate
+
+    regions = []
+    for sweep in range(sweeps):
+        for j in range(nreg):
+            first, m = ops.region_ms(j)
+            best, tried = first, 0
+            for key in keys:
+                if near_best(best, m):
+                    break
+                held = []
+                for _ in range(tries):
+                    h = ops.create(key, j)
+                    if h is None:
+                        break
+                    old = ops.current(key, j)
+                    ops.use(key, j, h)
+                    ms, _ = ops.region_ms(j)
+                    tried += 1
+                    if ms < best:
+                        best = ms
+                        held.append(old)
+                    else:
+                        ops.use(key, j, old)
+                        held.append(h)
+                    if near_best(best, m):
+                        break
+                for h in held:
+                    ops.release(h)
+            best_rate = best / m if best_rate is None else min(best_rate, best / m)
+            if sweep == sweeps - 1:
+                regions.append([j, round(first, 4), round(best, 4), tried])
+    return regions
+
+
+class _VmmRegionOps:
+    """search_regions' operations on one buffer's region-backed arrays: new
+    backings through dopt_vmm.h, pass 2 timed on one region through the C
+    ABI (a one-param layout of the region's length over the same memory)."""
+
+    def __init__(self, inf, back: Dict[str, _Backing], tensors, region_elems: int, launches: int, device):
+        from . import DOPT_MAX_HGROUPS as NH, hparams_array
+        self.inf, self.back, self.tensors = inf, back, tensors
+        self.region_elems, self.launches, self.device = region_elems, launches, device
+        self.es = {key: ES[inf["gd"]] if key == "grad" else ES[inf["pd"]] if key == "param" else 4
+                   for key in back}
+        self.layouts = {}
+        self.hp = hparams_array([(1e-3, 0.9, 0.999, 1e-8, 0.0)] * NH)
+        self.stream = torch.cuda.current_stream()
+
+    def _span(self, j):
+        lo = j * self.region_elems
+        return lo, min(self.region_elems, self.inf["n"] - lo)
+
+    def region_ms(self, j):
+        from . import dopt_build_ranges, dopt_init_state, dopt_step_apply, dopt_step_prepare, scaler_cfg
+        lo, m = self._span(j)
+        if m not in self.layouts:
+            inf = self.inf
+
+            class _P:
+                numel, param_dtype, grad_dtype = m, inf["pd"], inf["gd"]
+
+            Lr = dopt_build_ranges([_P()], 1, 0, 0)
+            self.layouts[m] = (Lr, torch.zeros(Lr.workspace_bytes, dtype=torch.uint8, device=self.device))
+        Lr, wsr = self.layouts[m]
+        rb = [{key: self.back[key].va + lo * self.es[key] for key in self.back}]
+        if self.inf["pd"] == "f32":
+            rb[0]["master"] = None
+        s = self.stream
+        dopt_init_state(Lr, rb, scaler_cfg(False, 1.0), wsr, s)
+        dopt_step_prepare(Lr, rb, self.hp, 0.0, wsr, s)
+        dopt_step_apply(Lr, rb, wsr, s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(self.launches):
+            dopt_step_apply(Lr, rb, wsr, s)
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / self.launches, m
+
+    def create(self, key, j):
+        from . import DoptError, dopt_vmm_create
+        try:
+            return dopt_vmm_create(self.back[key].region(j)[1])
+        except DoptError:
+            return None  # out of device memory for candidates
+
+    def current(self, key, j):
+        return self.back[key].handles[j]
+
+    def use(self, key, j, h):
+        self.back[key].replace(j, h)
+        lo, m = self._span(j)
+        self.tensors[key][lo:lo + m].zero_()
+
+    def release(self, h):
+        from . import dopt_vmm_release
+        torch.cuda.synchronize()
+        dopt_vmm_release(h)
+
+
 class DeviceArenas:
     """placement "sets": up to placement_tries whole arena sets, then array by
     array (below); "regions": the large buffers' arrays backed region by
@@ -257,21 +376,13 @@ class DeviceArenas:
 
     def _region_search(self, tries: int, launches: int, region_elems: int, sweeps: int, tol: float = 0.01):
         """Buffers of at least 4 regions get their five arrays (four for fp32
-        params) as reserved address ranges backed region by region; for every
-        region and array, up to `tries` candidate backings are mapped in turn
-        and pass 2 is timed on that region alone (a region-sized layout over
-        the same memory, through the C ABI); the fastest is kept.  Rejected
-        candidates are held until the region is done, so that each try gets
-        other physical memory.  A region whose time per element is within
-        `tol` (1%) of the best region seen so far is not searched further.  Smaller
-        buffers get plain allocations."""
-        from . import (DoptError, dopt_build_ranges, dopt_init_state, dopt_step_apply, dopt_step_prepare,
-                       dopt_vmm_create, dopt_vmm_granularity, dopt_vmm_release, hparams_array, scaler_cfg)
+        params) as reserved address ranges backed region by region, the
+        backings chosen by search_regions with pass 2 timed on one region at
+        a time; smaller buffers get plain allocations."""
+        from . import dopt_vmm_granularity
         gran = dopt_vmm_granularity(0)
         bufs = [self._alloc_buffer(inf) if inf["n"] < 4 * region_elems else {} for inf in self.info]
         ws = torch.zeros(self.layout.workspace_bytes, dtype=torch.uint8, device=self.device)
-        stream = torch.cuda.current_stream()
-        hp = hparams_array([(1e-3, 0.9, 0.999, 1e-8, 0.0)] * DOPT_MAX_HGROUPS)
         report = []
         self._backings = []
         for k, inf in enumerate(self.info):
@@ -279,81 +390,18 @@ class DeviceArenas:
             if n < 4 * region_elems:
                 continue
             keys = [key for key in KEYS if not (key == "master" and inf["pd"] == "f32")]
-            es = {"grad": ES[inf["gd"]], "param": ES[inf["pd"]], "master": 4, "exp_avg": 4, "exp_avg_sq": 4}
             dts = {"grad": inf["gd"], "param": inf["pd"], "master": "f32", "exp_avg": "f32", "exp_avg_sq": "f32"}
             back = {}
             bufs[k] = {key: None for key in KEYS}
             for key in keys:
-                back[key] = _Backing(n * es[key], region_elems * es[key], gran)
+                back[key] = _Backing(n * ES[dts[key]], region_elems * ES[dts[key]], gran)
                 bufs[k][key] = _tensor_over(back[key], n, dts[key])
                 bufs[k][key].zero_()
             self._backings.append(back)
-            nreg = -(-n // region_elems)
-            layouts = {}
-
-            class _P:
-                def __init__(self, numel):
-                    self.numel, self.param_dtype, self.grad_dtype = numel, inf["pd"], inf["gd"]
-
-            def region_ms(j):
-                lo = j * region_elems
-                m = min(region_elems, n - lo)
-                if m not in layouts:
-                    Lr = dopt_build_ranges([_P(m)], 1, 0, 0)
-                    layouts[m] = (Lr, torch.zeros(Lr.workspace_bytes, dtype=torch.uint8, device=self.device))
-                Lr, wsr = layouts[m]
-                rb = [{key: back[key].va + lo * es[key] for key in keys}]
-                if inf["pd"] == "f32":
-                    rb[0]["master"] = None
-                dopt_init_state(Lr, rb, scaler_cfg(False, 1.0), wsr, stream)
-                dopt_step_prepare(Lr, rb, hp, 0.0, wsr, stream)
-                dopt_step_apply(Lr, rb, wsr, stream)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(launches):
-                    dopt_step_apply(Lr, rb, wsr, stream)
-                b.record(stream)
-                torch.cuda.synchronize()
-                return a.elapsed_time(b) / launches, m
-
-            best_rate = float("inf")  # ms per element of the fastest region so far
-            regions = []
-            for sweep in range(sweeps):
-                for j in range(nreg):
-                    first, m = region_ms(j)
-                    best = first
-                    tried = 0
-                    for key in keys:
-                        if best / m <= (1.0 + tol) * best_rate:
-                            break
-                        held = []
-                        for _ in range(tries):
-                            try:
-                                h = dopt_vmm_create(back[key].region(j)[1])
-                            except DoptError:
-                                break  # out of device memory for candidates
-                            old = back[key].handles[j]
-                            back[key].replace(j, h)
-                            lo = j * region_elems
-                            bufs[k][key][lo:lo + m].zero_()
-                            ms, _ = region_ms(j)
-                            tried += 1
-                            if ms < best:
-                                best = ms
-                                held.append(old)
-                            else:
-                                back[key].replace(j, old)
-                                held.append(h)
-                            if best / m <= (1.0 + tol) * best_rate:
-                                break
-                        torch.cuda.synchronize()
-                        for h in held:
-                            dopt_vmm_release(h)
-                    best_rate = min(best_rate, best / m)
-                    if sweep == sweeps - 1:  # [region, ms before, ms after, candidates tried]
-                        regions.append([j, round(first, 4), round(best, 4), tried])
-            report.append({"buffer": k, "regions": nreg, "region_elems": region_elems, "sweeps": sweeps,
-                           "last_sweep": regions})
+            ops = _VmmRegionOps(inf, back, bufs[k], region_elems, launches, self.device)
+            regions = search_regions(ops, -(-n // region_elems), keys, tries, sweeps, tol)
+            report.append({"buffer": k, "regions": -(-n // region_elems), "region_elems": region_elems,
+                           "sweeps": sweeps, "last_sweep": regions})
         for b in bufs:
             for v in b.values():
                 if v is not None:
