@@ -32,6 +32,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -496,7 +497,6 @@ def setup(w, placement_tries: int, placement: str = "auto", region=(2, 0.01)):
 def placement_summary(A, seconds: float) -> dict:
     """The distribution of pass-2 times over the placements the search tried:
     whole arena sets, then each array's candidates with the others fixed."""
-    import statistics
     p = A.placement
     if p is None:
         return {"candidates": 1, "seconds": round(seconds, 3)}
@@ -567,7 +567,7 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
         flush.sum()
 
     def flushed_steps():
-        """K steps, each timed on its own right after evict(); total ms."""
+        """K steps, each timed on its own right after evict(); their ms."""
         ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
         for i in range(K):
@@ -576,10 +576,12 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
             step()
             ev_e[i].record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in zip(ev_s, ev_e))
+        return [a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]
 
+    per_step = None  # each step's ms where steps are timed one by one
     if flush_llc:
-        total_ms = flushed_steps()
+        per_step = flushed_steps()
+        total_ms = sum(per_step)
     else:
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
@@ -602,7 +604,8 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
     # the same steps with the last-level cache flushed before each (reported
     # beside the back-to-back figure; a training step runs after forward and
     # backward have passed far more than 256 MB through the cache)
-    flushed_ms = None if flush_llc else flushed_steps() / K
+    flushed = None if flush_llc else flushed_steps()
+    flushed_ms = None if flushed is None else sum(flushed) / K
     st = D.dopt_read_stats(L, A.workspace, stream)
     assert st["skipped"] == 0 and st["step_count"] == W + (2 if flush_llc else 3) * K, st
     skip = skip_step(L, A, step, K, stream) if w.dynamic_scale else None
@@ -620,6 +623,8 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
                    "arena_placement": placement_summary(A, t_alloc)},
         "hbm_GBps_step": round(gbps, 1),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
+        **({"ms_per_step_median": round(statistics.median(per_step), 5), "ms_per_step_best": round(min(per_step), 5)}
+           if per_step else {}),
         "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "launch_ms": round(apply_ms, 5), "launches_timed": K * APPLY_BATCH,
@@ -630,7 +635,9 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
     if flushed_ms is not None:
         res["llc_flushed"] = {"ms_per_step": round(flushed_ms, 5), "value": round(E / (flushed_ms * 1e-3) / 1e9, 3),
                               "unit": "Gparams/s", "hbm_GBps_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9, 1),
-                              "hbm_frac_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                              "hbm_frac_step": round(bytes_step / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "ms_per_step_median": round(statistics.median(flushed), 5),
+                              "ms_per_step_best": round(min(flushed), 5)}
     del A, bufs_c, flush
     return res
 
