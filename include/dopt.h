@@ -328,18 +328,25 @@ int dopt_step_apply(const dopt_layout *layout, const dopt_buffer_tensors *bufs, 
  * order and `scale` (e.g. 1/N for averaging, else 1) multiplies it once.
  *
  * chunks: host array of one device pointer per buffer; chunk j of buffer k
- * is the arena_numel elements at chunks[k] + j * arena_numel, element type
- * wire_dtype.  n_chunks must equal dp_size (one chunk per rank).  With hp
+ * is the arena_numel elements at chunks[k] + j * stride_k, element type
+ * wire_dtype, where stride_k = chunk_strides[k] (elements) or, with
+ * chunk_strides NULL, arena_numel (the chunks back to back).  A stride may
+ * exceed arena_numel (a receive buffer with room between chunks); the caller
+ * owns (n_chunks - 1) * stride_k + arena_numel elements at chunks[k], and the
+ * library reads only each chunk's arena_numel.  n_chunks must equal dp_size
+ * (one chunk per rank).  With hp
  * non-NULL the step's finalize runs too (as in dopt_step_prepare; then call
  * dopt_step_apply); with hp NULL only the grad-stats record is formed (as in
  * dopt_step_stats; then dopt_step_finalize after the cross-rank sum).
  * Errors: DOPT_ERR_INVALID (null or misaligned pointers, bad dtype,
- * n_chunks != dp_size, num_instances > 1, which [DP] §3.2 rules out),
- * DOPT_ERR_HIP.
+ * n_chunks != dp_size, num_instances > 1, which [DP] §3.2 rules out, a
+ * stride below arena_numel or whose bytes are not a multiple of
+ * DOPT_PTR_ALIGN), DOPT_ERR_HIP.
  */
 int dopt_reduce_prepare(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const void *const *chunks,
-                        int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp,
-                        int32_t n_hgroups, double max_grad_norm, void *workspace, hipStream_t stream);
+                        const int64_t *chunk_strides, int32_t wire_dtype, int32_t n_chunks, float scale,
+                        const dopt_hparams *hp, int32_t n_hgroups, double max_grad_norm, void *workspace,
+                        hipStream_t stream);
 
 /* Result of the pre-communication check of one bucket. */
 typedef struct dopt_bucket_check {

@@ -128,8 +128,8 @@ def _load():
         "dopt_step": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP, P(dopt_stats)], ctypes.c_int),
         "dopt_step_prepare": ([VP, P(dopt_buffer_tensors), P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
         "dopt_step_stats": ([VP, P(dopt_buffer_tensors), VP, VP], ctypes.c_int),
-        "dopt_reduce_prepare": ([VP, P(dopt_buffer_tensors), P(VP), I32, I32, ctypes.c_float, P(dopt_hparams), I32, D,
-                                 VP, VP], ctypes.c_int),
+        "dopt_reduce_prepare": ([VP, P(dopt_buffer_tensors), P(VP), P(I64), I32, I32, ctypes.c_float, P(dopt_hparams),
+                                 I32, D, VP, VP], ctypes.c_int),
         "dopt_check_grads": ([VP, I32, VP, D, VP, VP, VP], ctypes.c_int),
         "dopt_check_grads_noalloc": ([VP, I32, VP, D, VP, VP], ctypes.c_int),
         "dopt_step_finalize": ([VP, P(dopt_hparams), I32, D, VP, VP], ctypes.c_int),
@@ -407,21 +407,32 @@ def dopt_step_prepare(layout: Layout, bufs, hparams, max_grad_norm: float, works
 
 
 def dopt_reduce_prepare(layout: Layout, bufs, chunks: Sequence, wire_dtype: str, n_chunks: int, scale: float,
-                        hparams, max_grad_norm: float, workspace, stream=None):
-    """chunks: one device buffer per flat buffer holding n_chunks arenas back to back.
-    hparams None: stats only (finalize later with dopt_step_finalize)."""
+                        hparams, max_grad_norm: float, workspace, stream=None, chunk_strides: Optional[Sequence] = None):
+    """chunks: one device buffer per flat buffer holding n_chunks arenas,
+    chunk j at element j * stride (stride = chunk_strides[k], default
+    arena_numel: back to back).  hparams None: stats only (finalize later with
+    dopt_step_finalize)."""
     t = _marshal(layout, bufs)
     infos = layout.infos()
     if len(chunks) != len(infos):
         raise DoptError(DOPT_ERR_INVALID, f"{len(chunks)} chunk buffers, the layout has {len(infos)}")
-    ch = (ctypes.c_void_p * len(chunks))(*[_dev(c, f"buffer {k} chunks", wire_dtype, n_chunks * inf["arena_numel"])
-                                            for k, (c, inf) in enumerate(zip(chunks, infos))])
+    if chunk_strides is not None and len(chunk_strides) != len(infos):
+        raise DoptError(DOPT_ERR_INVALID, f"{len(chunk_strides)} chunk strides, the layout has {len(infos)} buffers")
+    strides = [int(chunk_strides[k]) if chunk_strides is not None else inf["arena_numel"]
+               for k, inf in enumerate(infos)]
+    for k, (st, inf) in enumerate(zip(strides, infos)):
+        if st < inf["arena_numel"]:
+            raise DoptError(DOPT_ERR_INVALID, f"buffer {k}: chunk stride {st} below the arena ({inf['arena_numel']})")
+    ch = (ctypes.c_void_p * len(chunks))(*[_dev(c, f"buffer {k} chunks", wire_dtype,
+                                                max(n_chunks - 1, 0) * st + inf["arena_numel"])
+                                            for k, (c, st, inf) in enumerate(zip(chunks, strides, infos))])
+    cs = None if chunk_strides is None else (ctypes.c_int64 * len(strides))(*strides)
     if hparams is None:
         hp, nh = None, 0
     else:
         hp = hparams if isinstance(hparams, ctypes.Array) else _hparams(hparams)
         nh = len(hp)
-    _check(_lib.dopt_reduce_prepare(layout.handle, t, ch, DTYPES[wire_dtype], n_chunks, scale, hp, nh,
+    _check(_lib.dopt_reduce_prepare(layout.handle, t, ch, cs, DTYPES[wire_dtype], n_chunks, scale, hp, nh,
                                     max_grad_norm, _ws(layout, workspace), _stream(stream)))
 
 

@@ -35,6 +35,18 @@ constexpr int kStatsMaxBlocks = 16384;
 // with 4 loads in flight, need the many-workgroup grid above.
 constexpr int kStatsMaxBlocksF32 = 256;
 constexpr int kReduceMaxBlocks = 1024;  // the fused reduce + pass 1
+// The fused reduce and the state copy of a large window are launched once per
+// kRangeTiles tiles (each launch grid-strides over its own range; the reduce's
+// launches write partials of their own).  Over thousands of iterations the
+// workgroups of one long launch drift apart and the pass's concurrent accesses
+// spread over more DRAM rows.  Measured on MI355X at 1.0e9 slots, in one
+// process: the reduce of 8 bf16 chunks 5.58 TB/s in ranges of 2^15 tiles,
+// 5.53 at 2^16, 5.45 at 2^14, 5.19 in one launch; the state export 6.11 /
+// 6.02 / 5.24-5.77 TB/s and the import 6.04-6.08 / 6.08 / 5.33-5.65 TB/s at
+// 2^15 / 2^16 / one launch.  Pass 2 gained 2-4% the same way on plain
+// allocations but nothing on the searched placements it runs on, so it keeps
+// one launch.
+constexpr int64_t kRangeTiles = 32768;
 constexpr int kApplyMaxBlocks = 256;
 constexpr int kCopyMaxBlocks = 256;  // state export / import
 constexpr int64_t kOneTileGridMax = 8192;  // tiles up to which a window counts as small
@@ -125,6 +137,7 @@ struct Buffer {
     std::vector<TileDesc> stats_tiles;
     TileBits bits{0, 0, {}};
     int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0, reduce_grid = 0;
+    int32_t reduce_launches = 0;  // the fused reduce's launches (kRangeTiles tiles each)
     int32_t partial_base = 0, reduce_partial_base = 0;  // first partial slot of pass 1 / the fused reduce
     int64_t ws_tiles = 0, ws_stats_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
     std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads

@@ -167,6 +167,8 @@ static void build_tiles(Buffer &B) {
     // the fused reduce + pass 1: one tile per workgroup on small windows
     B.reduce_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                     : std::min<int64_t>(n_tiles, kReduceMaxBlocks));
+    B.reduce_launches = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? 1
+                                                                        : (n_tiles + kRangeTiles - 1) / kRangeTiles);
     B.apply_grid = static_cast<int32_t>(n_tiles <= kApplyOneTileMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
@@ -219,7 +221,7 @@ static int build(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg 
         B.partial_base = partials;
         partials += B.stats_grid;
         B.reduce_partial_base = reduce_partials;
-        reduce_partials += B.reduce_grid;
+        reduce_partials += B.reduce_grid * B.reduce_launches;
         L.state_numel += B.shard_numel;
     }
     L.total_partials = partials;

@@ -563,12 +563,13 @@ template <int WD, int GD, int BATCH>
 __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict__ chunks, int64_t stride,
                                                         int32_t n_chunks, float scale, void *__restrict__ grad,
                                                         const TileDesc *__restrict__ tiles,
-                                                        const SegDesc *__restrict__ segs, int64_t n_tiles,
-                                                        const DevState *__restrict__ st, Partial *__restrict__ out) {
+                                                        const SegDesc *__restrict__ segs, int64_t t_begin,
+                                                        int64_t t_end, const DevState *__restrict__ st,
+                                                        Partial *__restrict__ out) {
     const float inv = st->inv_scale;
     double acc = 0.0;
     uint32_t zeros = 0;
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    for (int64_t t = t_begin + blockIdx.x; t < t_end; t += gridDim.x) {
         const TileDesc td = tiles[t];
         const int64_t i0 = t * kTile + int64_t(threadIdx.x) * kVec;
         float s[kVec];
@@ -966,11 +967,11 @@ template <int PD, bool IMPORT>
 __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param, float *__restrict__ master,
                                                       float *__restrict__ m, float *__restrict__ v,
                                                       const TileDesc *__restrict__ tiles,
-                                                      const SegDesc *__restrict__ segs, int64_t n_tiles,
-                                                      float *__restrict__ xm, float *__restrict__ xa,
+                                                      const SegDesc *__restrict__ segs, int64_t t_begin,
+                                                      int64_t t_end, float *__restrict__ xm, float *__restrict__ xa,
                                                       float *__restrict__ xv) {
     float *pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    for (int64_t t = t_begin + blockIdx.x; t < t_end; t += gridDim.x) {
         const TileDesc td = tiles[t];
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (cnt == 0) continue;
@@ -1183,33 +1184,49 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
     return launch_finish<FINALIZE>(L->total_partials, ws, stream, fa);
 }
 
+// One launch of the fused reduce over tiles [t0, t1) of a buffer; small
+// windows (one launch, one tile per workgroup) keep kReduceBatch chunk loads
+// in flight per thread, large ones one.
+struct ReduceLaunch {
+    dim3 grid;
+    const void *chunks;
+    int64_t stride;
+    int32_t n;
+    float scale;
+    void *grad;
+    const TileDesc *tiles;
+    const SegDesc *segs;
+    int64_t t0, t1;
+    bool small;
+    const DevState *st;
+    Partial *out;
+};
+
 template <int WD, int GD>
-static void launch_reduce_dt(dim3 grid, hipStream_t s, const void *chunks, int64_t stride, int32_t n, float scale,
-                             void *grad, const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles,
-                             const DevState *st, Partial *out) {
-    if (n_tiles <= kOneTileGridMax)
-        k_reduce_stats<WD, GD, kReduceBatch>
-            <<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+static void launch_reduce_dt(const ReduceLaunch &r, hipStream_t s) {
+    if (r.small)
+        k_reduce_stats<WD, GD, kReduceBatch><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad,
+                                                                       r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
     else
-        k_reduce_stats<WD, GD, 1><<<grid, kBlock, 0, s>>>(chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+        k_reduce_stats<WD, GD, 1><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad, r.tiles, r.segs,
+                                                            r.t0, r.t1, r.st, r.out);
 }
 
 template <int WD>
-static void launch_reduce_gd(int gd, dim3 grid, hipStream_t s, const void *chunks, int64_t stride, int32_t n,
-                             float scale, void *grad, const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles,
-                             const DevState *st, Partial *out) {
+static void launch_reduce_gd(int gd, const ReduceLaunch &r, hipStream_t s) {
     if (gd == DOPT_BF16)
-        launch_reduce_dt<WD, DOPT_BF16>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+        launch_reduce_dt<WD, DOPT_BF16>(r, s);
     else if (gd == DOPT_F16)
-        launch_reduce_dt<WD, DOPT_F16>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+        launch_reduce_dt<WD, DOPT_F16>(r, s);
     else
-        launch_reduce_dt<WD, DOPT_F32>(grid, s, chunks, stride, n, scale, grad, tiles, segs, n_tiles, st, out);
+        launch_reduce_dt<WD, DOPT_F32>(r, s);
 }
 
 // Fused local fp32 reduce + pass 1 over every buffer, then k_finish.
 template <bool FINALIZE>
-static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *const *chunks, int32_t wd,
-                         int32_t n_chunks, float scale, void *ws, hipStream_t stream, const FinalizeArgs &fa) {
+static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *const *chunks,
+                         const int64_t *strides, int32_t wd, int32_t n_chunks, float scale, void *ws,
+                         hipStream_t stream, const FinalizeArgs &fa) {
     const DevState *st = reinterpret_cast<const DevState *>(ws_ptr(ws, kWsState));
     Partial *part = reinterpret_cast<Partial *>(ws_ptr(ws, kWsPartials));
     for (size_t k = 0; k < L->buffers.size(); ++k) {
@@ -1217,21 +1234,33 @@ static int launch_reduce(const dopt_layout *L, const dopt_buffer_tensors *bufs, 
         const TileDesc *tiles = reinterpret_cast<const TileDesc *>(ws_ptr(ws, B.ws_tiles));
         const SegDesc *segs = reinterpret_cast<const SegDesc *>(ws_ptr(ws, B.ws_segs));
         const int64_t n_tiles = B.arena_numel / kTile;
-        const dim3 grid(B.reduce_grid);  // one partial per workgroup
-        Partial *out = part + B.reduce_partial_base;
+        ReduceLaunch r;
+        r.grid = dim3(B.reduce_grid);  // one partial per workgroup and launch
+        r.chunks = chunks[k];
+        r.stride = strides ? strides[k] : B.arena_numel;
+        r.n = n_chunks;
+        r.scale = scale;
         // the grad arena is this entry point's output (read-only everywhere else)
-        void *grad_out = const_cast<void *>(bufs[k].grad);
-        if (wd == DOPT_BF16)
-            launch_reduce_gd<DOPT_BF16>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
-                                        tiles, segs, n_tiles, st, out);
-        else if (wd == DOPT_F16)
-            launch_reduce_gd<DOPT_F16>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
-                                       tiles, segs, n_tiles, st, out);
-        else
-            launch_reduce_gd<DOPT_F32>(B.gd, grid, stream, chunks[k], B.arena_numel, n_chunks, scale, grad_out,
-                                       tiles, segs, n_tiles, st, out);
-        int rc = check_launch("launch k_reduce_stats");
-        if (rc) return rc;
+        r.grad = const_cast<void *>(bufs[k].grad);
+        r.tiles = tiles;
+        r.segs = segs;
+        r.small = n_tiles <= kOneTileGridMax;
+        r.st = st;
+        for (int32_t l = 0; l < B.reduce_launches; ++l) {
+            // every workgroup of every launch writes its partial (idle ones a
+            // zero), so the finish reads reduce_grid * reduce_launches of them
+            r.t0 = int64_t(l) * kRangeTiles;
+            r.t1 = r.small ? n_tiles : std::min(n_tiles, r.t0 + kRangeTiles);
+            r.out = part + B.reduce_partial_base + int64_t(l) * B.reduce_grid;
+            if (wd == DOPT_BF16)
+                launch_reduce_gd<DOPT_BF16>(B.gd, r, stream);
+            else if (wd == DOPT_F16)
+                launch_reduce_gd<DOPT_F16>(B.gd, r, stream);
+            else
+                launch_reduce_gd<DOPT_F32>(B.gd, r, stream);
+            int rc = check_launch("launch k_reduce_stats");
+            if (rc) return rc;
+        }
     }
     return launch_finish<FINALIZE>(L->total_reduce_partials, ws, stream, fa);
 }
@@ -1249,16 +1278,21 @@ static int state_copy(const dopt_layout *L, const dopt_buffer_tensors *bufs, flo
         const int64_t n_tiles = B.arena_numel / kTile;
         const dim3 grid(B.copy_grid);
         const dopt_buffer_tensors &b = bufs[k];
-        if (B.pd == DOPT_BF16)
-            k_state_copy<DOPT_BF16, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, b.master, b.exp_avg, b.exp_avg_sq,
-                                                                         tiles, segs, n_tiles, xm, xa, xv);
-        else if (B.pd == DOPT_F16)
-            k_state_copy<DOPT_F16, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, b.master, b.exp_avg, b.exp_avg_sq,
-                                                                        tiles, segs, n_tiles, xm, xa, xv);
-        else
-            k_state_copy<DOPT_F32, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, nullptr, b.exp_avg, b.exp_avg_sq,
-                                                                        tiles, segs, n_tiles, xm, xa, xv);
-        if ((rc = check_launch("launch k_state_copy"))) return rc;
+        // large windows in ranges of kRangeTiles tiles, small ones in one launch
+        const int64_t range = n_tiles <= kOneTileGridMax ? n_tiles : kRangeTiles;
+        for (int64_t t0 = 0; t0 < n_tiles; t0 += range) {
+            const int64_t t1 = std::min(n_tiles, t0 + range);
+            if (B.pd == DOPT_BF16)
+                k_state_copy<DOPT_BF16, IMPORT><<<grid, kBlock, 0, stream>>>(
+                    b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs, t0, t1, xm, xa, xv);
+            else if (B.pd == DOPT_F16)
+                k_state_copy<DOPT_F16, IMPORT><<<grid, kBlock, 0, stream>>>(
+                    b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs, t0, t1, xm, xa, xv);
+            else
+                k_state_copy<DOPT_F32, IMPORT><<<grid, kBlock, 0, stream>>>(b.param, nullptr, b.exp_avg, b.exp_avg_sq,
+                                                                            tiles, segs, t0, t1, xm, xa, xv);
+            if ((rc = check_launch("launch k_state_copy"))) return rc;
+        }
     }
     return DOPT_OK;
 }
@@ -1421,7 +1455,7 @@ int dopt_step_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, con
 }
 
 int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, const void *const *chunks,
-                        int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp, int32_t n_hgroups,
+                        const int64_t *chunk_strides, int32_t wire_dtype, int32_t n_chunks, float scale, const dopt_hparams *hp, int32_t n_hgroups,
                         double max_grad_norm, void *ws, hipStream_t stream) {
     int rc = check_bufs(L, bufs, ws, true);
     if (rc != DOPT_OK) return rc;
@@ -1431,16 +1465,26 @@ int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, c
         return fail(DOPT_ERR_INVALID, "bad wire dtype");
     if (n_chunks != L->dp_size) return fail(DOPT_ERR_INVALID, "n_chunks must equal dp_size (one chunk per rank)");
     if (!chunks) return fail(DOPT_ERR_INVALID, "null chunk array");
-    for (size_t k = 0; k < L->buffers.size(); ++k)
+    const int64_t wbytes = wire_dtype == DOPT_F32 ? 4 : 2;
+    for (size_t k = 0; k < L->buffers.size(); ++k) {
         if (!chunks[k] || !aligned(chunks[k]))
             return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": null or unaligned chunk pointer");
+        // every chunk starts DOPT_PTR_ALIGN-aligned and holds a whole arena
+        if (chunk_strides && (chunk_strides[k] < L->buffers[k].arena_numel ||
+                              (chunk_strides[k] * wbytes) % DOPT_PTR_ALIGN != 0))
+            return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": chunk stride " +
+                                              std::to_string(chunk_strides[k]) + " below the arena (" +
+                                              std::to_string(L->buffers[k].arena_numel) +
+                                              " elements) or not a multiple of " + std::to_string(DOPT_PTR_ALIGN) +
+                                              " bytes");
+    }
     FinalizeArgs a;
     std::memset(&a, 0, sizeof a);
     if (hp) {
         if ((rc = build_finalize_args(L, hp, n_hgroups, max_grad_norm, a))) return rc;
-        return launch_reduce<true>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
+        return launch_reduce<true>(L, bufs, chunks, chunk_strides, wire_dtype, n_chunks, scale, ws, stream, a);
     }
-    return launch_reduce<false>(L, bufs, chunks, wire_dtype, n_chunks, scale, ws, stream, a);
+    return launch_reduce<false>(L, bufs, chunks, chunk_strides, wire_dtype, n_chunks, scale, ws, stream, a);
 }
 
 int dopt_check_grads(const dopt_layout *L, int32_t k, const void *grad, double thr, dopt_bucket_check *out, void *ws,

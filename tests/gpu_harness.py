@@ -480,7 +480,11 @@ def _pick_samples(O: oracle.Layout, k: int, n_rand: int, seed: int) -> np.ndarra
         bk = O.bucket(k, b)
         if bk["shard"] > 0:
             wins += [bk["arena_offset"], bk["arena_offset"] + bk["shard"] - 1]
-    tiles = np.unique(np.concatenate([ends, np.array(wins, np.int64)]) // 2048)
+    # and the tiles on both sides of every multiple of 2^26 slots, where a
+    # pass launched over ranges of the arena (the fused reduce's ranges are
+    # multiples of it) starts a new range
+    cuts = np.arange(1 << 26, int(O.buffer(k)["window_numel"]), 1 << 26, dtype=np.int64)
+    tiles = np.unique(np.concatenate([ends, np.array(wins, np.int64), cuts - 1, cuts]) // 2048)
     tb = []
     for tl in tiles.tolist():
         lo, hi = tl * 2048, tl * 2048 + 2048

@@ -121,6 +121,29 @@ def test_reduce_chunks_and_exports(L):
     _err(lambda: D.dopt_state_import(L, t, ok.double(), ok, ok, 0), "import master", "dtype")
 
 
+def test_reduce_chunk_strides(L):
+    """A stride below the arena, a chunk buffer too short for its stride, a
+    stride list of the wrong length (binding), and a stride whose bytes are
+    not a multiple of 256 (the library's own check, reached here with raw
+    addresses before anything touches a device)."""
+    t = D.tensors(L, _bufs(L))
+    infos = L.infos()
+    ar = [inf["arena_numel"] for inf in infos]
+    raw = [4096] * len(infos)
+    _err(lambda: D.dopt_reduce_prepare(L, t, raw, "bf16", 4, 1.0, None, 1.0, 4096, chunk_strides=ar[:2]),
+         "2 chunk strides")
+    _err(lambda: D.dopt_reduce_prepare(L, t, raw, "bf16", 4, 1.0, None, 1.0, 4096,
+                                       chunk_strides=[ar[0], ar[1] - 128, ar[2]]), "buffer 1", "below the arena")
+    ch = [torch.zeros(4 * a, dtype=torch.bfloat16) for a in ar]  # back to back: too short for a wider stride
+    _err(lambda: D.dopt_reduce_prepare(L, t, ch, "bf16", 4, 1.0, None, 1.0, 4096,
+                                       chunk_strides=[ar[0] + 128, ar[1], ar[2]]), "buffer 0 chunks", "at least")
+    _err(lambda: D.dopt_reduce_prepare(L, t, raw, "bf16", 4, 1.0, None, 1.0, 4096,
+                                       chunk_strides=[ar[0], ar[1], ar[2] + 8]), "buffer 2", "chunk stride",
+         "multiple of 256 bytes")
+    _err(lambda: D.dopt_reduce_prepare(L, t, raw, "f32", 4, 1.0, None, 1.0, 4096,
+                                       chunk_strides=[ar[0] + 32, ar[1], ar[2]]), "buffer 0", "chunk stride")
+
+
 def test_noalloc_check_refuses_buffers_beyond_its_static_scratch():
     # 2^34 elements: 2^20 check tiles of 16 B = 16 MiB of partials plus the
     # bucket table, more than the library's static scratch holds.  The library

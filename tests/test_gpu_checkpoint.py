@@ -141,8 +141,9 @@ def test_reshard_8_to_4_to_3_matches_one_rank(scaler, max_norm, inf_at):
 
 
 def test_export_import_large_window_matches_oracle():
-    """A window of more than 8192 tiles takes the fixed-grid, grid-stride path."""
-    params = [ParamSpec("big", 20_000_003, "bf16", "bf16"), ParamSpec("n", 5000, "f32", "f32", 0, 1),
+    """A window of more than 32768 tiles: the fixed-grid, grid-stride path,
+    launched over more than one range of tiles."""
+    params = [ParamSpec("big", 70_000_003, "bf16", "bf16"), ParamSpec("n", 5000, "f32", "f32", 0, 1),
               ParamSpec("h", 777, "bf16", "bf16", 1, 0)]
     w = [synth.fill_normal(p.param_dtype, p.numel, 5, synth.weight_stream(i), 0, 0.02) for i, p in enumerate(params)]
     g = [synth.fill_normal(p.grad_dtype, p.numel, 5, synth.grad_stream(i), 1, 1e-2) for i, p in enumerate(params)]
@@ -150,7 +151,7 @@ def test_export_import_large_window_matches_oracle():
     ranks.init(w)
     ranks.step(g, HPS, 1.0)
     L, A = ranks.layouts[0], ranks.arenas[0]
-    assert L.buffer(0)["arena_numel"] // 2048 > 8192
+    assert L.buffer(0)["arena_numel"] // 2048 > 32768
     run = OracleRun(params, 1, 0, 0, arena_numel=[A.info[k]["n"] for k in range(L.num_buffers)])
     _oracle_view(run, ranks, 0)
     n = L.state_numel
