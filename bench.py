@@ -52,12 +52,12 @@ REGION_ELEMS = 1 << 27  # arena elements per placement region
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 106,561.86 KiB * 2.0 + WRITE_SIZE 213,557.77 KiB * 1.0, averaged over 379 dispatches
+    # FETCH_SIZE 106,551.73 KiB * 2.0 + WRITE_SIZE 213,550.53 KiB * 1.0, averaged over 523 dispatches
     # (profiles/k_apply_gpt2-small_kernel_trace.md)
-    "gpt2-small": {"src": "d6256e3464ba7df1", "bytes_per_launch": 436921853},
-    # FETCH_SIZE 46,269,124.20 KiB * 2.0 + WRITE_SIZE 92,128,333.61 KiB * 1.0, averaged over the 37
-    # dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
-    "dense-7b": {"src": "d6256e3464ba7df1", "bytes_per_launch": 189098579978},
+    "gpt2-small": {"src": "9c8c297420f59ba1", "bytes_per_launch": 436893686},
+    # FETCH_SIZE 46,269,131.61 KiB * 2.0 + WRITE_SIZE 92,127,626.50 KiB * 1.0, averaged over the 37
+    # full-window dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
+    "dense-7b": {"src": "9c8c297420f59ba1", "bytes_per_launch": 189097871073},
 }
 
 
