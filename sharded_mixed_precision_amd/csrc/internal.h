@@ -138,6 +138,7 @@ struct Buffer {
     TileBits bits{0, 0, {}};
     int32_t stats_grid = 0, apply_grid = 0, copy_grid = 0, reduce_grid = 0;
     int32_t reduce_launches = 0;  // the fused reduce's launches (kRangeTiles tiles each)
+    bool apply_bnd = false;       // pass 2 in k_apply_bnd: a grid-stride window with boundary tiles
     int32_t partial_base = 0, reduce_partial_base = 0;  // first partial slot of pass 1 / the fused reduce
     int64_t ws_tiles = 0, ws_stats_tiles = 0, ws_segs = 0;  // byte offsets in the workspace
     std::vector<CheckBucket> chk;       // per bucket, for dopt_check_grads

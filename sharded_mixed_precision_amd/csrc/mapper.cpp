@@ -171,6 +171,9 @@ static void build_tiles(Buffer &B) {
                                                                         : (n_tiles + kRangeTiles - 1) / kRangeTiles);
     B.apply_grid = static_cast<int32_t>(n_tiles <= kApplyOneTileMax ? n_tiles
                                                                    : std::min<int64_t>(n_tiles, kApplyMaxBlocks));
+    B.apply_bnd = false;
+    if (B.apply_grid < n_tiles)
+        for (const TileDesc &td : B.tiles) B.apply_bnd = B.apply_bnd || !(td.seg_count & kTileFull);
     B.copy_grid = static_cast<int32_t>(n_tiles <= kOneTileGridMax ? n_tiles
                                                                   : std::min<int64_t>(n_tiles, kCopyMaxBlocks));
 }

@@ -957,6 +957,111 @@ __global__ void __launch_bounds__(kBlock) k_apply(const void *__restrict__ grad,
     }
 }
 
+// Pass 2 for a large window (grid-stride) that holds boundary tiles: a tile
+// whose segments share one hyper-group updates the 8 elements it already
+// holds in registers, as a full tile does, and stores only the owned ones.
+// In k_apply a boundary tile walks its elements one at a time, re-reading
+// each from the tile; on a grid-stride launch the workgroups that draw such
+// tiles fall behind and the launch waits for the slowest (the Llama-3-70B
+// rank of N=64 has 381 boundary tiles in 538,283: pass 2 5.18 ms in k_apply,
+// 5.10 ms here).  A separate kernel, so that k_apply (every small window, and
+// the large ones without boundary tiles) keeps its own code; this one holds
+// more registers, capped at 64 so that it never drops below 8 waves per SIMD.
+template <int PD, int GD>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8)))
+k_apply_bnd(const void *__restrict__ grad, void *__restrict__ param, float *__restrict__ master,
+            float *__restrict__ m, float *__restrict__ v, const TileDesc *__restrict__ tiles,
+            const SegDesc *__restrict__ segs, int64_t n_tiles, const StepRec *__restrict__ rec, TileBits tb) {
+    const int skip = rec->skip;
+    const float inv = rec->inv_scale;
+    const int clip_on = rec->clip_on;
+    const float clip = rec->clip;
+    const int hpre = tb.on ? tb.hg : 0;
+    const Hp h0 = load_hp(rec, hpre);
+    if (skip) return;
+    float *__restrict__ pm = (PD == DOPT_F32) ? static_cast<float *>(param) : master;
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const int64_t tile0 = t * kTile;
+        const int32_t lane = threadIdx.x;
+        const auto rg = tile_rsrc(static_cast<const char *>(grad) + tile0 * Elem<GD>::kBytes, kTile * Elem<GD>::kBytes);
+        const auto rp = tile_rsrc(pm + tile0, kTile * 4);
+        const auto rm = tile_rsrc(m + tile0, kTile * 4);
+        const auto rv = tile_rsrc(v + tile0, kTile * 4);
+        const auto rq = tile_rsrc(static_cast<char *>(param) + tile0 * Elem<PD>::kBytes, kTile * Elem<PD>::kBytes);
+        float g[kVec], p[kVec], a[kVec], b[kVec];
+        Elem<GD>::bload8(rg, lane, g);
+        bload8f(rp, lane, p);
+        bload8f(rm, lane, a);
+        bload8f(rv, lane, b);
+        TileDesc td{0, kTileFull | (hpre << kTileHgShift)};
+        if (!tb.on || ((tb.w[t >> 5] >> (t & 31)) & 1u)) td = tiles[t];
+        const int32_t cnt = td.seg_count & kTileCountMask;
+        const bool full = (td.seg_count & kTileFull) != 0;
+        int hg = (td.seg_count >> kTileHgShift) & kTileHgMask;
+        uint32_t own = 0xffu;  // the lane's elements that belong to a param
+        if (!full) {
+            // the segments that meet the tile (disjoint; a wave-uniform loop)
+            // give the lane's owned elements
+            const int32_t l0 = lane * kVec;  // the lane's first element within the tile
+            own = 0;
+            hg = cnt > 0 ? segs[td.seg_first].hgroup : hpre;
+            bool one_hg = true;
+            for (int32_t sg = td.seg_first; sg < td.seg_first + cnt; ++sg) {
+                const int32_t lo = static_cast<int32_t>(max(segs[sg].start - tile0, int64_t(0)));
+                const int32_t hi = static_cast<int32_t>(min(segs[sg].end - tile0, int64_t(kTile)));
+                one_hg = one_hg && segs[sg].hgroup == hg;
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) own |= (lo <= l0 + j && l0 + j < hi) ? 1u << j : 0u;
+            }
+            if (!one_hg) {
+                // segments of several hyper-groups meet in the tile: each owned
+                // element on its own with its segment's scalars, as in k_apply
+                const int64_t e0 = tile0 + int64_t(lane) * kVec;
+                for (int32_t sg = td.seg_first; sg < td.seg_first + cnt; ++sg) {
+                    const int64_t s0 = segs[sg].start, s1 = segs[sg].end;
+                    const Hp hs = load_hp(rec, segs[sg].hgroup);
+#pragma unroll 1
+                    for (int j = 0; j < kVec; ++j) {
+                        if (s0 <= e0 + j && e0 + j < s1) {
+                            const int32_t o4 = lane * 32 + j * 4;
+                            float pj = bld4(rp, o4), aj = bld4(rm, o4), bj = bld4(rv, o4);
+                            adamw(Elem<GD>::bload1(rg, lane, j), pj, aj, bj, inv, clip_on, clip, hs);
+                            bst4(rp, o4, pj);
+                            bst4(rm, o4, aj);
+                            bst4(rv, o4, bj);
+                            if (PD != DOPT_F32) Elem<PD>::bstore1(rq, lane, j, pj);
+                        }
+                    }
+                }
+                continue;
+            }
+        }
+        // one hyper-group: all 8 elements are updated (an element of no param
+        // is computed and dropped)
+        const Hp h = hg == hpre ? h0 : load_hp(rec, hg);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) adamw(g[j], p[j], a[j], b[j], inv, clip_on, clip, h);
+        if (full) {
+            bstore8f(rp, lane, p);
+            bstore8f(rm, lane, a);
+            bstore8f(rv, lane, b);
+            if (PD != DOPT_F32) Elem<PD>::bstore8(rq, lane, p);
+        } else {
+            // only the owned elements are stored; the others keep their bytes
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                if ((own >> j) & 1u) {
+                    const int32_t o4 = lane * 32 + j * 4;
+                    bst4(rp, o4, p[j]);
+                    bst4(rm, o4, a[j]);
+                    bst4(rv, o4, b[j]);
+                    if (PD != DOPT_F32) Elem<PD>::bstore1(rq, lane, j, p[j]);
+                }
+            }
+        }
+    }
+}
+
 // ---- model-space state export / import -------------------------------------------
 //
 // Every shard element e of the arena corresponds to export slot
@@ -1092,21 +1197,30 @@ static int check_bufs(const dopt_layout *L, const dopt_buffer_tensors *bufs, con
     return DOPT_OK;
 }
 
-template <int PD>
-static void launch_apply_gd(int gd, dim3 grid, hipStream_t s, const dopt_buffer_tensors &b, const TileDesc *tiles,
+template <int PD, int GD>
+static void launch_apply_dt(bool bnd, dim3 grid, hipStream_t s, const dopt_buffer_tensors &b, const TileDesc *tiles,
                             const SegDesc *segs, int64_t n_tiles, const StepRec *rec, const TileBits &tb) {
+    if (bnd)
+        k_apply_bnd<PD, GD><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
+                                                    n_tiles, rec, tb);
+    else
+        k_apply<PD, GD><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
+                                                n_tiles, rec, tb);
+}
+
+template <int PD>
+static void launch_apply_gd(int gd, bool bnd, dim3 grid, hipStream_t s, const dopt_buffer_tensors &b,
+                            const TileDesc *tiles, const SegDesc *segs, int64_t n_tiles, const StepRec *rec,
+                            const TileBits &tb) {
     switch (gd) {
     case DOPT_BF16:
-        k_apply<PD, DOPT_BF16><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                     n_tiles, rec, tb);
+        launch_apply_dt<PD, DOPT_BF16>(bnd, grid, s, b, tiles, segs, n_tiles, rec, tb);
         break;
     case DOPT_F16:
-        k_apply<PD, DOPT_F16><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                    n_tiles, rec, tb);
+        launch_apply_dt<PD, DOPT_F16>(bnd, grid, s, b, tiles, segs, n_tiles, rec, tb);
         break;
     default:
-        k_apply<PD, DOPT_F32><<<grid, kBlock, 0, s>>>(b.grad, b.param, b.master, b.exp_avg, b.exp_avg_sq, tiles, segs,
-                                                    n_tiles, rec, tb);
+        launch_apply_dt<PD, DOPT_F32>(bnd, grid, s, b, tiles, segs, n_tiles, rec, tb);
         break;
     }
 }
@@ -1589,13 +1703,13 @@ int dopt_step_apply(const dopt_layout *L, const dopt_buffer_tensors *bufs, void 
         const dim3 grid(B.apply_grid);
         switch (B.pd) {
         case DOPT_BF16:
-            launch_apply_gd<DOPT_BF16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
+            launch_apply_gd<DOPT_BF16>(B.gd, B.apply_bnd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         case DOPT_F16:
-            launch_apply_gd<DOPT_F16>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
+            launch_apply_gd<DOPT_F16>(B.gd, B.apply_bnd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         default:
-            launch_apply_gd<DOPT_F32>(B.gd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
+            launch_apply_gd<DOPT_F32>(B.gd, B.apply_bnd, grid, stream, bufs[k], tiles, segs, n_tiles, rec, B.bits);
             break;
         }
         if ((rc = check_launch("launch k_apply"))) return rc;

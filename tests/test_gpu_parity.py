@@ -169,6 +169,24 @@ def test_split_api_large_window():
     H.run_full(H.Case("split-large", params, 2, 1, steps=3), split_steps=(1, 3), half_steps=(2,))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dt,n,r", [(("bf16", "bf16"), 1, 0), (("f16", "f32"), 2, 1)], ids=["bf16-n1", "f16-f32-n2"])
+def test_large_window_with_boundary_tiles(dt, n, r):
+    """A window of more than 16384 tiles (pass 2 grid-strides over it) whose
+    params meet inside tiles: tiles shared by two params of one hyper-group
+    (updated from registers and stored element by element) and by params of
+    two hyper-groups (updated element by element with each one's scalars);
+    every element compared for 3 steps."""
+    import sharded_mixed_precision_amd as D
+    pd, gd = dt
+    sizes = [(20_000_003, 0), (3_000_001, 0), (9_999_999, 1), (7_000_001, 2), (333, 2)]
+    params = [ParamSpec(f"p{i}", k * n, pd, gd, 0, hg) for i, (k, hg) in enumerate(sizes)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
+    L = D.dopt_build_ranges(params, n, r)
+    assert L.buffer(0)["arena_numel"] // D.DOPT_ARENA_ALIGN > 16384
+    H.run_full(H.Case(f"bnd-{pd}-{gd}-n{n}", params, n, r, steps=3, hparams=hps))
+
+
 def test_many_tiny_params():
     """About 3000 params of 1 to 100 elements (64-element aligned starts): nearly
     every tile is a boundary tile holding up to 32 shards, the worst case of
