@@ -46,18 +46,22 @@ APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
 SMALL_WINDOW = 64 << 20  # shard elements up to which the default step counts are large
 REGION_ELEMS = 1 << 27  # arena elements per placement region
 
-# HBM traffic of k_apply measured with rocprofv3 PMC counters (FETCH_SIZE,
+# HBM traffic of pass 2 (k_apply; k_apply_bnd for Llama-3-70B, whose window has
+# boundary tiles) measured with rocprofv3 PMC counters (FETCH_SIZE,
 # WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
 # reported only while the kernel source is the one that was measured.
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 106,551.73 KiB * 2.0 + WRITE_SIZE 213,550.53 KiB * 1.0, averaged over 523 dispatches
+    # FETCH_SIZE 106,536.62 KiB * 2.0 + WRITE_SIZE 213,529.97 KiB * 1.0, averaged over 523 dispatches
     # (profiles/k_apply_gpt2-small_kernel_trace.md)
-    "gpt2-small": {"src": "9c8c297420f59ba1", "bytes_per_launch": 436893686},
-    # FETCH_SIZE 46,269,131.61 KiB * 2.0 + WRITE_SIZE 92,127,626.50 KiB * 1.0, averaged over the 37
+    "gpt2-small": {"src": "c58a129972cd4076", "bytes_per_launch": 436841694},
+    # FETCH_SIZE 46,269,094.93 KiB * 2.0 + WRITE_SIZE 92,127,731.18 KiB * 1.0, averaged over the 37
     # full-window dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
-    "dense-7b": {"src": "9c8c297420f59ba1", "bytes_per_launch": 189097871073},
+    "dense-7b": {"src": "c58a129972cd4076", "bytes_per_launch": 189097903139},
+    # k_apply_bnd: FETCH_SIZE 7,569,698.31 KiB * 2.0 + WRITE_SIZE 15,072,198.56 KiB * 1.0, averaged over 37
+    # dispatches (profiles/k_apply_llama3-70b_kernel_trace.md)
+    "llama3-70b": {"src": "c58a129972cd4076", "bytes_per_launch": 30936673464},
 }
 
 
@@ -625,7 +629,8 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         **({"ms_per_step_median": round(statistics.median(per_step), 5), "ms_per_step_best": round(min(per_step), 5)}
            if per_step else {}),
-        "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2)", "achieved": round(ach, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2; k_apply_bnd on grid-stride windows with boundary tiles)",
+                     "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "launch_ms": round(apply_ms, 5), "launches_timed": K * APPLY_BATCH,
                      "algorithmic_bytes_per_launch": apply_bytes},
