@@ -1110,23 +1110,53 @@ __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param,
             }
             continue;
         }
-        for (int j = 0; j < kVec; ++j) {
-            const int64_t e = t * kTile + int64_t(j) * kBlock + threadIdx.x;
-            int32_t s = td.seg_first;
-            if (!(td.seg_count & kTileFull)) {
-                while (s < td.seg_first + cnt && !(segs[s].start <= e && e < segs[s].end)) ++s;
-                if (s == td.seg_first + cnt) continue;  // alignment gap, padding or arena tail
+        // A boundary tile: the segments that meet it (a wave-uniform loop, so
+        // their fields are scalar loads) give each of the lane's elements its
+        // export offset, and, as in a full tile, every load is issued before
+        // the first store.  Elements in no segment (alignment gaps, padding,
+        // the arena tail) are neither read nor written.
+        const int64_t e0 = t * kTile + threadIdx.x;
+        int64_t dx[kVec];
+        uint32_t own = 0;
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) dx[j] = 0;
+        for (int32_t sg = td.seg_first; sg < td.seg_first + cnt; ++sg) {
+            const int64_t s0 = segs[sg].start, s1 = segs[sg].end, d = segs[sg].xoff - s0;
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t e = e0 + int64_t(j) * kBlock;
+                if (s0 <= e && e < s1) {
+                    dx[j] = d;
+                    own |= 1u << j;
+                }
             }
-            const int64_t x = segs[s].xoff + (e - segs[s].start);
-            if (IMPORT) {
-                pm[e] = xm[x];
-                m[e] = xa[x];
-                v[e] = xv[x];
-                if (PD != DOPT_F32) Elem<PD>::store1(param, e, xm[x]);
-            } else {
-                xm[x] = pm[e];
-                xa[x] = m[e];
-                xv[x] = v[e];
+        }
+        float a[kVec], b[kVec], c[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            a[j] = b[j] = c[j] = 0.0f;
+            if ((own >> j) & 1u) {
+                const int64_t e = e0 + int64_t(j) * kBlock;
+                a[j] = IMPORT ? xm[e + dx[j]] : pm[e];
+                b[j] = IMPORT ? xa[e + dx[j]] : m[e];
+                c[j] = IMPORT ? xv[e + dx[j]] : v[e];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            if ((own >> j) & 1u) {
+                const int64_t e = e0 + int64_t(j) * kBlock;
+                if (IMPORT) {
+                    pm[e] = a[j];
+                    m[e] = b[j];
+                    v[e] = c[j];
+                    if (PD != DOPT_F32) Elem<PD>::store1(param, e, a[j]);
+                } else {
+                    xm[e + dx[j]] = a[j];
+                    xa[e + dx[j]] = b[j];
+                    xv[e + dx[j]] = c[j];
+                }
             }
         }
     }
