@@ -46,8 +46,8 @@ APPLY_BATCH = 10  # pass-2 launches between one pair of events (roofline timing)
 SMALL_WINDOW = 64 << 20  # shard elements up to which the default step counts are large
 REGION_ELEMS = 1 << 27  # arena elements per placement region
 
-# HBM traffic of pass 2 (k_apply; k_apply_bnd for Llama-3-70B, whose window has
-# boundary tiles) measured with rocprofv3 PMC counters (FETCH_SIZE,
+# HBM traffic of pass 2 (k_apply, or k_apply_bnd for Llama-3-70B, whose window
+# has boundary tiles) measured with rocprofv3 PMC counters (FETCH_SIZE,
 # WRITE_SIZE) and scaled by the same counters on a plain copy of known size;
 # reported only while the kernel source is the one that was measured.
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
@@ -526,6 +526,17 @@ def placement_summary(A, seconds: float) -> dict:
     return out
 
 
+def pass2_kernels(A) -> str:
+    """The pass-2 kernel of each buffer, as the library chose it (k_apply_bnd
+    for a grid-stride window that holds boundary tiles)."""
+    names = []
+    for info in A.info:
+        name = "k_apply_bnd" if info.get("apply_bnd") else "k_apply"
+        if name not in names:
+            names.append(name)
+    return " + ".join(names)
+
+
 def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placement: str = "auto",
                  region=(2, 0.01)) -> dict:
     """Time K back-to-back steps of one workload (or K steps each after an
@@ -629,8 +640,7 @@ def measure_step(w, steps, warmup, placement_tries: int, flush_llc: bool, placem
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         **({"ms_per_step_median": round(statistics.median(per_step), 5), "ms_per_step_best": round(min(per_step), 5)}
            if per_step else {}),
-        "roofline": {"bound": "hbm", "kernel": "k_apply (pass 2; k_apply_bnd on grid-stride windows with boundary tiles)",
-                     "achieved": round(ach, 1),
+        "roofline": {"bound": "hbm", "kernel": pass2_kernels(A) + " (pass 2)", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "launch_ms": round(apply_ms, 5), "launches_timed": K * APPLY_BATCH,
                      "algorithmic_bytes_per_launch": apply_bytes},

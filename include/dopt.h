@@ -154,6 +154,10 @@ typedef struct dopt_buffer_info {
     int64_t window_numel;   /* sum of the rank's window sizes */
     int64_t arena_numel;    /* window_numel rounded up to DOPT_ARENA_ALIGN: size of every arena array */
     int64_t shard_numel;    /* param elements inside the rank's windows */
+    int32_t apply_bnd;      /* 1: pass 2 runs k_apply_bnd, which updates boundary tiles (params meeting
+                               inside a 2048-element tile) from registers: a window of more than 16384 tiles
+                               (grid-stride) that holds one; 0: k_apply */
+    int32_t reserved;
 } dopt_buffer_info;
 
 typedef struct dopt_bucket_info {

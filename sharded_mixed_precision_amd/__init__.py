@@ -59,7 +59,8 @@ class dopt_range(ctypes.Structure):
 class dopt_buffer_info(ctypes.Structure):
     _fields_ = [("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
                 ("n_params", ctypes.c_int32), ("numel", ctypes.c_int64), ("numel_unpadded", ctypes.c_int64),
-                ("window_numel", ctypes.c_int64), ("arena_numel", ctypes.c_int64), ("shard_numel", ctypes.c_int64)]
+                ("window_numel", ctypes.c_int64), ("arena_numel", ctypes.c_int64), ("shard_numel", ctypes.c_int64),
+                ("apply_bnd", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class dopt_bucket_info(ctypes.Structure):
@@ -267,7 +268,7 @@ class Layout:
     def buffer(self, k: int) -> Dict:
         o = dopt_buffer_info()
         _check(_lib.dopt_layout_buffer(self._h, k, ctypes.byref(o)))
-        return {name: getattr(o, name) for name, _ in o._fields_}
+        return {name: getattr(o, name) for name, _ in o._fields_ if name != "reserved"}
 
     def bucket(self, k: int, b: int) -> Dict:
         o = dopt_bucket_info()

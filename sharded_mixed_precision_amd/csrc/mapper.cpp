@@ -326,6 +326,8 @@ int dopt_layout_buffer(const dopt_layout *L, int32_t k, dopt_buffer_info *out) {
     out->window_numel = B.window_numel;
     out->arena_numel = B.arena_numel;
     out->shard_numel = B.shard_numel;
+    out->apply_bnd = B.apply_bnd ? 1 : 0;
+    out->reserved = 0;
     return DOPT_OK;
 }
 

@@ -96,6 +96,46 @@ def test_mapper_matches_oracle_random(seed):
         _compare(params, N, r, bucket_size, int(seed % 5 == 0))
 
 
+def _expected_apply_bnd(B, k) -> int:
+    """From the oracle's segments: a window of more than 16384 2048-element
+    tiles (pass 2 grid-strides over it) in which some tile is not covered by
+    one segment (params meeting inside it, a gap, the ragged tail)."""
+    s, ln, _ = B.segments(k)
+    tiles = -(-B.buffer(k)["window_numel"] // 2048)
+    full = sum(max(0, (e // 2048) - (-(-a // 2048))) for a, e in zip(s.tolist(), (s + ln).tolist()))
+    return int(tiles > 16384 and full < tiles)
+
+
+@pytest.mark.parametrize("case", ["workloads", "boundary-layouts"])
+def test_pass2_kernel_choice_follows_the_tiles(case):
+    """dopt_buffer_info.apply_bnd (pass 2 in k_apply_bnd) is set exactly for
+    grid-stride windows that hold a boundary tile: the Llama-3-70B rank, whose
+    windows all cut params, and not dense-7B or Llama-3-8B (whose shards fill
+    their tiles) or the small windows."""
+    d = _dopt()
+    if case == "workloads":
+        layouts = [(PARAM_LISTS[w.model](), w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
+                   for w in WORKLOADS.values()]
+    else:
+        sizes = [(20_000_003, 0), (3_000_001, 0), (9_999_999, 1), (7_000_001, 2), (333, 2)]
+        layouts = []
+        for n, r, scale in ((1, 0, 1), (2, 1, 2), (1, 0, 0.5)):  # the last: 19.5M slots, one tile per workgroup
+            params = [ParamSpec(f"p{i}", int(k * scale), "bf16", "bf16", 0, hg) for i, (k, hg) in enumerate(sizes)]
+            layouts.append((params, n, r, 0, 0))
+    got = []
+    for params, N, r, bucket_size, busbw in layouts:
+        A = d.dopt_build_ranges(params, N, r, bucket_size, busbw)
+        B = oracle.Layout(params, N, r, bucket_size, busbw)
+        for k in range(A.num_buffers):
+            assert A.buffer(k)["apply_bnd"] == _expected_apply_bnd(B, k), (len(params), N, r, k)
+            got.append(A.buffer(k)["apply_bnd"])
+    if case == "workloads":
+        # tiny, gpt2-small, llama3-8b (two buffers), dense-7b, llama3-70b
+        assert got == [0, 0, 0, 0, 0, 1], got
+    else:
+        assert got == [1, 1, 0], got
+
+
 def test_mapper_errors():
     d = _dopt()
     ok = [ParamSpec("a", 10, "bf16", "bf16")]

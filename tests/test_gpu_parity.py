@@ -183,7 +183,7 @@ def test_large_window_with_boundary_tiles(dt, n, r):
     params = [ParamSpec(f"p{i}", k * n, pd, gd, 0, hg) for i, (k, hg) in enumerate(sizes)]
     hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (3e-4, 0.8, 0.99, 1e-6, 0.0), (2e-3, 0.95, 0.9999, 1e-8, 0.1)]
     L = D.dopt_build_ranges(params, n, r)
-    assert L.buffer(0)["arena_numel"] // D.DOPT_ARENA_ALIGN > 16384
+    assert L.buffer(0)["arena_numel"] // D.DOPT_ARENA_ALIGN > 16384 and L.buffer(0)["apply_bnd"] == 1
     H.run_full(H.Case(f"bnd-{pd}-{gd}-n{n}", params, n, r, steps=3, hparams=hps))
 
 
