@@ -19,8 +19,8 @@ it is measured:
   range backed region by region (``dopt_vmm.h``; regions of 2^27 elements).
   For every region and array, candidate backings are mapped in turn and
   pass 2 is timed on that region alone; the fastest is kept.  Per region the
-  times fall into two groups (about 5.4 and 6.1 TB/s); two sweeps bring every
-  region to the faster one.  The search holds at most one region of memory per
+  times fall into two groups (about 5.4 and 6.1 TB/s); enough candidates and
+  sweeps bring every region to the faster one (see DeviceArenas).  The search holds at most one region of memory per
   candidate and took 0.3-9 s for the Llama-3 ranks and the 108 GB dense-7B
   state with 2 sweeps, 8 candidates and a 1% tolerance (40-50 s for dense-7B
   with 3 sweeps, 12 candidates and 0.3%, which gained another 0.5%).
@@ -252,11 +252,22 @@ class DeviceArenas:
     """placement "sets": up to placement_tries whole arena sets, then array by
     array (below); "regions": the large buffers' arrays backed region by
     region through dopt_vmm.h, each region's backing chosen by timing pass 2
-    on that region (region_search)."""
+    on that region (region_search), with up to placement_tries candidates per
+    array and region.
+
+    How many candidates the region search needs depends on where the
+    process's memory comes from.  Five 2^30-element arrays allocated first
+    in a process started with every region in the slow group (5.1 TB/s for
+    pass 2); 8 candidates, 2 sweeps and a 1% tolerance stayed there (the
+    first region found no fast backing, and the others were then within the
+    tolerance of it), while 16 candidates, 3 sweeps and 0.3% reached the fast
+    group (6.1 TB/s) in 4-9 s.  The same arrays allocated after 128 GiB of
+    other memory started in the fast group.  The defaults below are the
+    sweeps and tolerance that escaped; pass placement_tries of 12 or more."""
 
     def __init__(self, layout: Layout, device: str = "cuda", placement_tries: int = 1,
                  timed_launches: int = 5, placement: str = "sets", region_elems: int = 1 << 27,
-                 region_sweeps: int = 2, region_tolerance: float = 0.01):
+                 region_sweeps: int = 3, region_tolerance: float = 0.003):
         self.layout = layout
         self.device = device
         self.info = []
