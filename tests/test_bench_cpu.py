@@ -70,3 +70,27 @@ def test_placement_summary_of_region_search():
     assert out["kind"] == "regions" and b["regions"] == 3 and b["region_ms_kept"] == 1.41
     assert b["region_ms_before_last_sweep"] == 1.52 and b["candidates_last_sweep"] == 7
     assert b["fastest_region_ms"] == 0.19 and b["slowest_region_ms"] == 0.61
+
+
+def test_pass2_kernel_label_follows_the_layout():
+    """The roofline names the pass-2 kernel the library chose for each buffer
+    (dopt_buffer_info.apply_bnd), each kernel once, in buffer order."""
+    import sharded_mixed_precision_amd as D
+    from synth import PARAM_LISTS, WORKLOADS
+
+    class A:
+        def __init__(self, L):
+            self.info = L.infos()
+
+    labels = {}
+    for name in ("dense-7b", "llama3-8b", "llama3-70b"):
+        w = WORKLOADS[name]
+        L = D.dopt_build_ranges(PARAM_LISTS[w.model](), w.dp_size, w.dp_rank, w.bucket_size, w.pad_for_high_busbw)
+        labels[name] = bench.pass2_kernels(A(L))
+    assert labels == {"dense-7b": "k_apply", "llama3-8b": "k_apply", "llama3-70b": "k_apply_bnd"}
+
+
+def test_traffic_entries_cover_the_headline():
+    # counters for the headline workload are stored (reported while their
+    # source hash is the library's)
+    assert "dense-7b" in bench.MEASURED_TRAFFIC
