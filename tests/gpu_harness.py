@@ -65,6 +65,9 @@ class Case:
     wire: str = "bf16"
     reduce_scale: float = 1.0
     reduce_split: bool = False
+    # slots after each received chunk, filled with NaN and never read: chunk
+    # j of an n-slot arena starts at j * (n + chunk_pad)
+    chunk_pad: int = 0
     placement_tries: int = 1  # DeviceArenas placement search (1: plain allocation)
     placement: str = "sets"  # "regions": large buffers backed region by region (dopt_vmm.h)
     region_elems: int = 1 << 27
@@ -104,6 +107,15 @@ def host_chunks(case: Case, k: int, n: int, step: int, out=None):
     """case.chunks received chunks of an n-slot arena, back to back, in the wire dtype."""
     return synth.fill_normal(case.wire, case.chunks * n, case.seed, synth.chunk_stream(k), step, case.grad_sigma,
                              zero_frac=case.zero_frac, out=out)
+
+
+def padded_chunks(case: Case, packed: torch.Tensor, n: int) -> torch.Tensor:
+    """The chunks at a stride of n + case.chunk_pad, the gaps filled with NaN."""
+    stride = n + case.chunk_pad
+    out = torch.full((case.chunks * stride,), math.nan, dtype=packed.dtype)
+    for j in range(case.chunks):
+        out[j * stride:j * stride + n] = packed[j * n:(j + 1) * n]
+    return out
 
 
 def inf_position(case: Case, O: oracle.Layout):
@@ -227,13 +239,14 @@ class DeviceRun:
             self.dev_chunks = [torch.empty(t.numel(), dtype=t.dtype, device="cuda") for t in host_chunks]
         for d, t in zip(self.dev_chunks, host_chunks):
             d.copy_(t)
+        strides = [inf["arena_numel"] + c.chunk_pad for inf in self.L.infos()] if c.chunk_pad else None
         if c.reduce_split:
             self.D.dopt_reduce_prepare(self.L, self.A.bufs, self.dev_chunks, c.wire, c.chunks, c.reduce_scale, None,
-                                       c.max_norm, self.A.workspace, self.stream)
+                                       c.max_norm, self.A.workspace, self.stream, chunk_strides=strides)
             self.D.dopt_step_finalize(self.L, c.hparams, c.max_norm, self.A.workspace, self.stream)
         else:
             self.D.dopt_reduce_prepare(self.L, self.A.bufs, self.dev_chunks, c.wire, c.chunks, c.reduce_scale,
-                                       c.hparams, c.max_norm, self.A.workspace, self.stream)
+                                       c.hparams, c.max_norm, self.A.workspace, self.stream, chunk_strides=strides)
         self.D.dopt_step_apply(self.L, self.A.bufs, self.A.workspace, self.stream)
         return self.D.dopt_read_stats(self.L, self.A.workspace, self.stream)
 
@@ -276,9 +289,12 @@ def run_full(case: Case, split_steps: Sequence[int] = (), half_steps: Sequence[i
         for k, b in enumerate(hp):
             if case.chunks:
                 ch = host_chunks(case, k, b["n"], s)
+                if case.chunk_pad:
+                    ch = padded_chunks(case, ch, b["n"])
                 chunks.append(ch)
                 oracle.lib().or_reduce_chunks(orc.L.handle, k, ch.data_ptr(), oracle.DTYPES[case.wire], case.chunks,
-                                              b["n"], case.reduce_scale, 0, b["n"], b["grad"].ctypes.data)
+                                              b["n"] + case.chunk_pad, case.reduce_scale, 0, b["n"],
+                                              b["grad"].ctypes.data)
                 continue
             g = host_grads(case, k, b["gd"], b["n"], s)
             if pos is not None and s == case.inf_step and pos[0] == k:

@@ -43,6 +43,30 @@ def test_reduce_mixed_buffers_odd_windows():
     H.run_full(H.Case("reduce-mixed", params, 128, 77, 0, steps=2, chunks=128, wire="bf16"))
 
 
+@pytest.mark.parametrize("wire,pad", [("bf16", 384), ("f32", 2048 + 64)], ids=["bf16", "f32"])
+def test_reduce_padded_chunk_stride(wire, pad):
+    """Chunks received at a stride wider than the arena (a caller's receive
+    buffer with room between chunks), the gaps filled with NaN: the reduced
+    grads, the statistics and the step after them match the oracle reading
+    the same buffer at the same stride, so no gap slot is read."""
+    params = [ParamSpec("a", 50000, "bf16", "f32"), ParamSpec("n", 300, "f32", "f32"),
+              ParamSpec("b", 7777, "f16", "f16", 0, 1)]
+    hps = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (5e-4, 0.9, 0.99, 1e-8, 0.0)]
+    H.run_full(H.Case(f"reduce-stride-{wire}", params, 4, 1, 0, steps=2, hparams=hps, chunks=4, wire=wire,
+                      chunk_pad=pad))
+
+
+@pytest.mark.timeout(600)
+def test_reduce_padded_chunk_stride_large_window():
+    """A 70M-slot window (several range launches of the reduce) with its 2
+    chunks 2176 slots apart beyond the arena, every slot compared."""
+    import sharded_mixed_precision_amd as D
+    params = [ParamSpec("w", 139_999_991, "bf16", "f32"), ParamSpec("x", 777, "bf16", "f32")]
+    L = D.dopt_build_ranges(params, 2, 1, 0)
+    assert L.buffer(0)["arena_numel"] // D.DOPT_ARENA_ALIGN > 32768
+    H.run_full(H.Case("reduce-stride-large", params, 2, 1, 0, steps=2, chunks=2, wire="bf16", chunk_pad=2176))
+
+
 @pytest.mark.timeout(600)
 def test_reduce_llama3_8b_sampled():
     # the Llama-3-8B rank (N=8, r=5, ~1.0e9 fp32 grad slots): 8 bf16 chunks per slot
