@@ -170,7 +170,8 @@ def test_split_api_large_window():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("dt,n,r", [(("bf16", "bf16"), 1, 0), (("f16", "f32"), 2, 1)], ids=["bf16-n1", "f16-f32-n2"])
+@pytest.mark.parametrize("dt,n,r", [(("bf16", "bf16"), 1, 0), (("f16", "f32"), 2, 1), (("f32", "f32"), 1, 0)],
+                         ids=["bf16-n1", "f16-f32-n2", "f32-n1"])
 def test_large_window_with_boundary_tiles(dt, n, r):
     """A window of more than 16384 tiles (pass 2 grid-strides over it) whose
     params meet inside tiles: tiles shared by two params of one hyper-group
