@@ -8,10 +8,12 @@
 // The step is bound by HBM bandwidth (about 1 flop per byte), so no matrix
 // cores are involved.  Each pass streams the arena arrays once with 16-byte
 // loads and stores: one 256-thread workgroup per 2048-element tile, 8
-// consecutive elements per thread, grid-stride over the tiles.  Tiles that lie
-// inside one param's shard (nearly all) take a branch-free path; tiles that
-// hold a shard boundary, a 64-element alignment gap or the arena tail test
-// each element against the few segments that overlap them.
+// consecutive elements per thread, grid-stride over the tiles (the fused
+// reduce and the state copy of a large window in launches of kRangeTiles
+// tiles).  Tiles that lie inside one param's shard (nearly all) take a
+// branch-free path; tiles that hold a shard boundary, a 64-element alignment
+// gap or the arena tail test each element against the few segments that
+// overlap them (pass 2 of a large window with such tiles in k_apply_bnd).
 //
 // Arithmetic is IEEE fp32 in the order stated at adamw() below: the library
 // is built with contraction off, correctly rounded sqrt and division, and
@@ -1613,14 +1615,15 @@ int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, c
     for (size_t k = 0; k < L->buffers.size(); ++k) {
         if (!chunks[k] || !aligned(chunks[k]))
             return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": null or unaligned chunk pointer");
-        // every chunk starts DOPT_PTR_ALIGN-aligned and holds a whole arena
-        if (chunk_strides && (chunk_strides[k] < L->buffers[k].arena_numel ||
+        // every chunk starts DOPT_PTR_ALIGN-aligned and holds a whole arena;
+        // strides up to 2^40 elements keep every chunk offset in 64 bits
+        if (chunk_strides && (chunk_strides[k] < L->buffers[k].arena_numel || chunk_strides[k] > (int64_t(1) << 40) ||
                               (chunk_strides[k] * wbytes) % DOPT_PTR_ALIGN != 0))
             return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": chunk stride " +
                                               std::to_string(chunk_strides[k]) + " below the arena (" +
                                               std::to_string(L->buffers[k].arena_numel) +
-                                              " elements) or not a multiple of " + std::to_string(DOPT_PTR_ALIGN) +
-                                              " bytes");
+                                              " elements), above 2^40 or not a multiple of " +
+                                              std::to_string(DOPT_PTR_ALIGN) + " bytes");
     }
     FinalizeArgs a;
     std::memset(&a, 0, sizeof a);

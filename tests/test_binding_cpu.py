@@ -142,6 +142,8 @@ def test_reduce_chunk_strides(L):
          "multiple of 256 bytes")
     _err(lambda: D.dopt_reduce_prepare(L, t, raw, "f32", 4, 1.0, None, 1.0, 4096,
                                        chunk_strides=[ar[0] + 32, ar[1], ar[2]]), "buffer 0", "chunk stride")
+    _err(lambda: D.dopt_reduce_prepare(L, t, raw, "bf16", 4, 1.0, None, 1.0, 4096,
+                                       chunk_strides=[ar[0], (1 << 41), ar[2]]), "buffer 1", "above 2^40")
 
 
 def test_noalloc_check_refuses_buffers_beyond_its_static_scratch():
