@@ -113,11 +113,98 @@ def cpu_baseline(workload, seconds: float):
         os.sched_setaffinity(0, mask)
     res["host"] = host_cpu()
     res["host"]["pinned_core"] = min(mask)
+    threads = min(16, len(mask))
+    if threads > 1:
+        th = _cpu_threaded(workload, seconds / 2, threads)
+        if th is not None:
+            res["threaded"] = th
     return res
 
 
-def _cpu_baseline(workload, seconds: float):
+def _large_sample(workload):
+    """The oracle's inputs for the first 2^24 arena slots of buffer 0 of a
+    large rank window (seeded like the GPU run's inputs); None for a window
+    of at most 2^25 shard elements."""
     import numpy as np
+    import oracle
+    import synth
+    from tests.oracle_harness import to_bits
+
+    params = synth.PARAM_LISTS[workload.model]()
+    O = oracle.Layout(params, workload.dp_size, workload.dp_rank, workload.bucket_size)
+    if sum(O.buffer(k)["shard_numel"] for k in range(O.num_buffers)) <= (1 << 25):
+        return None  # a small window: the baseline runs whole oracle steps instead
+    lib = oracle.lib()
+    b0 = O.buffer(0)
+    pd, gd = {0: "f32", 1: "bf16", 2: "f16"}[b0["param_dtype"]], {0: "f32", 1: "bf16", 2: "f16"}[b0["grad_dtype"]]
+    n = min(1 << 24, b0["window_numel"])
+    g = to_bits(synth.fill_normal(gd, n, 0, synth.grad_stream(0), 1, workload.grad_sigma)).copy()
+    p = to_bits(synth.fill_normal(pd, n, 0, synth.weight_stream(0), 0, 0.02)).copy()
+    master = np.zeros(n, np.float32)
+    if pd == "bf16":
+        lib.or_bf16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
+    elif pd == "f16":
+        lib.or_f16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
+    return {"O": O, "lib": lib, "pd": pd, "gd": gd, "n": n, "g": g, "p": p, "master": master,
+            "m": np.zeros(n, np.float32), "v": np.zeros(n, np.float32), "hg": np.zeros(n, np.int32)}
+
+
+def _cpu_threaded(workload, seconds: float, threads: int):
+    """Context beside the oracle, not the oracle itself: the oracle's range
+    functions on `threads` disjoint slices of the same large-window sample,
+    run on host threads (the library releases the interpreter lock), the
+    statistics of the slices added in slice order.  None for small windows."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+
+    S = _large_sample(workload)
+    if S is None:
+        return None
+    lib, n = S["lib"], S["n"]
+    ES_ = {"f32": 4, "bf16": 2, "f16": 2}
+    eg, ep = ES_[S["gd"]], ES_[S["pd"]]
+    cut = [(n * i // threads) // 2048 * 2048 for i in range(threads)] + [n]
+    ranges = [(cut[i], cut[i + 1]) for i in range(threads) if cut[i + 1] > cut[i]]
+    hp = [(workload.lr, workload.beta1, workload.beta2, workload.eps, workload.weight_decay)]
+    sc = oracle.make_scaler(workload.dynamic_scale, workload.initial_scale)
+    t = ctypes.c_int64(0)
+    inv = lib.or_inv_scale(ctypes.byref(sc))
+
+    def stats(r):
+        st = oracle.Stats()
+        lib.or_grad_stats_range(S["O"].handle, 0, S["g"].ctypes.data, inv, r[0], r[1], ctypes.byref(st))
+        return st
+
+    def apply(r, s):
+        lo, cnt = r[0], r[1] - r[0]
+        lib.or_apply_elems(oracle.DTYPES[S["pd"]], oracle.DTYPES[S["gd"]], cnt, S["hg"].ctypes.data + 4 * lo,
+                           S["g"].ctypes.data + eg * lo, S["master"].ctypes.data + 4 * lo, S["m"].ctypes.data + 4 * lo,
+                           S["v"].ctypes.data + 4 * lo, S["p"].ctypes.data + ep * lo, ctypes.byref(s))
+
+    steps, t0 = 0, time.perf_counter()
+    with ThreadPoolExecutor(len(ranges)) as pool:
+        while True:
+            parts = list(pool.map(stats, ranges))
+            st = oracle.Stats()
+            for q in parts:
+                st.sumsq += q.sumsq
+                st.zeros += q.zeros
+                st.found_inf = st.found_inf or q.found_inf
+            s = oracle.Scalars()
+            lib.or_decide(ctypes.byref(st), ctypes.byref(sc), ctypes.byref(t), oracle.make_hparams(hp), 1,
+                          workload.max_grad_norm, ctypes.byref(s))
+            list(pool.map(lambda r: apply(r, s), ranges))
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(n * steps / el / 1e9, 6), "unit": "Gparams/s", "threads": len(ranges),
+            "kind": "the oracle's range functions on disjoint slices of the sample, on host threads; "
+                    "context beside the oracle, not the oracle",
+            "sample": f"first {n} arena slots of buffer 0, {steps} stats+update passes in {el:.1f}s"}
+
+
+def _cpu_baseline(workload, seconds: float):
     import oracle
     import synth
     from tests.oracle_harness import OracleRun, to_bits
@@ -144,26 +231,15 @@ def _cpu_baseline(workload, seconds: float):
                           f"1 thread"}
     # large windows: the oracle's per-element stats + update on the first
     # 2^24 arena slots of buffer 0 (same arithmetic per element as a full step)
-    lib = oracle.lib()
-    b0 = O.buffer(0)
-    pd, gd = {0: "f32", 1: "bf16", 2: "f16"}[b0["param_dtype"]], {0: "f32", 1: "bf16", 2: "f16"}[b0["grad_dtype"]]
-    n = min(1 << 24, b0["window_numel"])
-    g = to_bits(synth.fill_normal(gd, n, 0, synth.grad_stream(0), 1, workload.grad_sigma)).copy()
-    p = to_bits(synth.fill_normal(pd, n, 0, synth.weight_stream(0), 0, 0.02)).copy()
-    master = np.zeros(n, np.float32)
-    if pd == "bf16":
-        lib.or_bf16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
-    elif pd == "f16":
-        lib.or_f16_to_f32_n(p.ctypes.data, master.ctypes.data, n)
-    m = np.zeros(n, np.float32)
-    v = np.zeros(n, np.float32)
-    hg = np.zeros(n, np.int32)
+    S = _large_sample(workload)
+    lib, n, pd, gd = S["lib"], S["n"], S["pd"], S["gd"]
+    g, p, master, m, v, hg = S["g"], S["p"], S["master"], S["m"], S["v"], S["hg"]
     sc = oracle.make_scaler(workload.dynamic_scale, workload.initial_scale)
     t = ctypes.c_int64(0)
     steps, t0 = 0, time.perf_counter()
     while True:
         st = oracle.Stats()
-        lib.or_grad_stats_range(O.handle, 0, g.ctypes.data, lib.or_inv_scale(ctypes.byref(sc)), 0, n,
+        lib.or_grad_stats_range(S["O"].handle, 0, g.ctypes.data, lib.or_inv_scale(ctypes.byref(sc)), 0, n,
                                 ctypes.byref(st))
         s = oracle.Scalars()
         lib.or_decide(ctypes.byref(st), ctypes.byref(sc), ctypes.byref(t), oracle.make_hparams(hp), 1,
