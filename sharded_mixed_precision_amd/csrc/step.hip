@@ -548,9 +548,12 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 // time (the adds stay in chunk order); the chunks are read once, so they are
 // loaded nontemporally.  Small windows take BATCH = kReduceBatch (latency
 // bound: the more loads in flight per thread, the better); large ones
-// BATCH = 1, which measured faster on MI355X once the whole chip is busy
-// (fewer distinct DRAM rows open at a time).
+// BATCH = kReduceBatchLarge.  On MI355X with the whole chip busy, 2 loads
+// per thread read 64 bf16 chunks 6% faster than 1 and 8 chunks with an fp32
+// grad write as fast; 4, or 2 on twice the workgroups, put so many requests
+// in flight that the mixed read and write streams slowed down.
 constexpr int kReduceBatch = 8;
+constexpr int kReduceBatchLarge = 2;
 
 template <int GD>
 __device__ __forceinline__ float stored_value(float x);
@@ -1332,7 +1335,7 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
 
 // One launch of the fused reduce over tiles [t0, t1) of a buffer; small
 // windows (one launch, one tile per workgroup) keep kReduceBatch chunk loads
-// in flight per thread, large ones one.
+// in flight per thread, large ones kReduceBatchLarge.
 struct ReduceLaunch {
     dim3 grid;
     const void *chunks;
@@ -1354,8 +1357,8 @@ static void launch_reduce_dt(const ReduceLaunch &r, hipStream_t s) {
         k_reduce_stats<WD, GD, kReduceBatch><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad,
                                                                        r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
     else
-        k_reduce_stats<WD, GD, 1><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad, r.tiles, r.segs,
-                                                            r.t0, r.t1, r.st, r.out);
+        k_reduce_stats<WD, GD, kReduceBatchLarge><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad,
+                                                                            r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
 }
 
 template <int WD>
