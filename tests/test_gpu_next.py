@@ -68,6 +68,21 @@ def test_reduce_padded_chunk_stride_large_window():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,wire", [(1, "bf16"), (3, "bf16"), (3, "f32")], ids=["1-bf16", "3-bf16", "3-f32"])
+def test_reduce_large_window_odd_chunk_counts(n, wire):
+    """A window past the one-tile-per-workgroup grid (the large-window reduce,
+    which issues its chunk loads two at a time) reduced from an odd number of
+    chunks, so that the last chunk is loaded alone (with one chunk, every
+    one); every slot compared."""
+    import sharded_mixed_precision_amd as D
+    params = [ParamSpec("w", 59_999_989, "bf16", "f32"), ParamSpec("x", 4097, "bf16", "f32")]
+    r = n // 2
+    L = D.dopt_build_ranges(params, n, r, 0)
+    assert L.buffer(0)["arena_numel"] // D.DOPT_ARENA_ALIGN > 8192
+    H.run_full(H.Case(f"reduce-odd-{n}-{wire}", params, n, r, 0, steps=2, chunks=n, wire=wire))
+
+
+@pytest.mark.timeout(600)
 def test_reduce_llama3_8b_sampled():
     # the Llama-3-8B rank (N=8, r=5, ~1.0e9 fp32 grad slots): 8 bf16 chunks per slot
     case = H.case_from_workload(synth.WORKLOADS["llama3-8b"])
