@@ -345,7 +345,8 @@ int dopt_step_apply(const dopt_layout *layout, const dopt_buffer_tensors *bufs, 
  * Errors: DOPT_ERR_INVALID (null or misaligned pointers, bad dtype,
  * n_chunks != dp_size, num_instances > 1, which [DP] §3.2 rules out, a
  * stride below arena_numel, above 2^40 elements or whose bytes are not a
- * multiple of DOPT_PTR_ALIGN), DOPT_ERR_HIP.
+ * multiple of DOPT_PTR_ALIGN, n_chunks strides of 2^62 bytes or more),
+ * DOPT_ERR_HIP.
  */
 int dopt_reduce_prepare(const dopt_layout *layout, const dopt_buffer_tensors *bufs, const void *const *chunks,
                         const int64_t *chunk_strides, int32_t wire_dtype, int32_t n_chunks, float scale,

@@ -1618,8 +1618,7 @@ int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, c
     for (size_t k = 0; k < L->buffers.size(); ++k) {
         if (!chunks[k] || !aligned(chunks[k]))
             return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": null or unaligned chunk pointer");
-        // every chunk starts DOPT_PTR_ALIGN-aligned and holds a whole arena;
-        // strides up to 2^40 elements keep every chunk offset in 64 bits
+        // every chunk starts DOPT_PTR_ALIGN-aligned and holds a whole arena
         if (chunk_strides && (chunk_strides[k] < L->buffers[k].arena_numel || chunk_strides[k] > (int64_t(1) << 40) ||
                               (chunk_strides[k] * wbytes) % DOPT_PTR_ALIGN != 0))
             return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": chunk stride " +
@@ -1627,6 +1626,13 @@ int dopt_reduce_prepare(const dopt_layout *L, const dopt_buffer_tensors *bufs, c
                                               std::to_string(L->buffers[k].arena_numel) +
                                               " elements), above 2^40 or not a multiple of " +
                                               std::to_string(DOPT_PTR_ALIGN) + " bytes");
+        // the n_chunks chunks span less than 2^62 bytes, so every element and
+        // byte offset the kernel forms from them fits in 64 bits
+        const int64_t stride = chunk_strides ? chunk_strides[k] : L->buffers[k].arena_numel;
+        if (stride > (int64_t(1) << 62) / (wbytes * int64_t(n_chunks)))
+            return fail(DOPT_ERR_INVALID, "buffer " + std::to_string(k) + ": " + std::to_string(n_chunks) +
+                                              " chunks at a stride of " + std::to_string(stride) +
+                                              " elements span 2^62 bytes or more");
     }
     FinalizeArgs a;
     std::memset(&a, 0, sizeof a);

@@ -146,6 +146,17 @@ def test_reduce_chunk_strides(L):
                                        chunk_strides=[ar[0], (1 << 41), ar[2]]), "buffer 1", "above 2^40")
 
 
+def test_reduce_chunk_span_beyond_64_bit_offsets():
+    """2^22 chunks (one per rank) at a stride of 2^40 bf16 elements would span
+    2^63 bytes: the library refuses before forming any chunk offset (raw
+    addresses, nothing touches a device)."""
+    n = 1 << 22
+    Lb = D.dopt_build_ranges([ParamSpec("a", 5000, "bf16", "bf16")], n, 7, 0)
+    t = D.tensors(Lb, [{"grad": 4096, "param": 4096, "master": 4096, "exp_avg": 4096, "exp_avg_sq": 4096}])
+    _err(lambda: D.dopt_reduce_prepare(Lb, t, [4096], "bf16", n, 1.0, None, 1.0, 4096, chunk_strides=[1 << 40]),
+         "buffer 0", f"{n} chunks", "2^62 bytes")
+
+
 def test_noalloc_check_refuses_buffers_beyond_its_static_scratch():
     # 2^34 elements: 2^20 check tiles of 16 B = 16 MiB of partials plus the
     # bucket table, more than the library's static scratch holds.  The library
