@@ -224,10 +224,10 @@ typedef struct dopt_scaler_cfg {
     int32_t kind;            /* DOPT_SCALER_CONSTANT or DOPT_SCALER_DYNAMIC */
     int32_t hysteresis;      /* dynamic: overflows tolerated before a backoff (>= 1) */
     int64_t growth_interval; /* dynamic: clean steps between growths (>= 1) */
-    double initial_scale;    /* > 0 */
-    double growth_factor;    /* dynamic, > 1 */
+    double initial_scale;    /* finite, > 0, and 1/initial_scale a finite nonzero fp32 number */
+    double growth_factor;    /* dynamic, finite, > 1 */
     double backoff_factor;   /* dynamic, in (0, 1) */
-    double min_scale;        /* dynamic, > 0 */
+    double min_scale;        /* dynamic, as initial_scale */
 } dopt_scaler_cfg;
 
 /*
@@ -441,7 +441,9 @@ typedef struct dopt_state_scalars {
     int64_t hysteresis_tracker;
 } dopt_state_scalars;
 
-/* Read / overwrite the scalar state (host struct); both synchronize `stream`. */
+/* Read / overwrite the scalar state (host struct); both synchronize `stream`.
+ * _set: loss_scale as dopt_scaler_cfg.initial_scale, step_count >= 0, else
+ * DOPT_ERR_INVALID before anything is written. */
 int dopt_state_scalars_get(const dopt_layout *layout, const void *workspace, hipStream_t stream,
                            dopt_state_scalars *out);
 int dopt_state_scalars_set(const dopt_layout *layout, void *workspace, hipStream_t stream,

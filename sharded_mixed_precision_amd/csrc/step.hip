@@ -1498,6 +1498,15 @@ static int scratch_on_current_device(char **out) {
     return DOPT_OK;
 }
 
+// A loss scale the step can run with: positive and finite, with a
+// reciprocal (the factor every grad is unscaled by, kept in fp32) that is a
+// finite nonzero fp32 number.
+static bool usable_scale(double s) {
+    if (!(s > 0.0) || !std::isfinite(s)) return false;
+    const float inv = static_cast<float>(1.0 / s);
+    return inv > 0.0f && std::isfinite(inv);
+}
+
 }  // namespace dopt
 
 using namespace dopt;
@@ -1509,11 +1518,12 @@ int dopt_init_state(const dopt_layout *L, const dopt_buffer_tensors *bufs, const
     int rc = check_bufs(L, bufs, ws, false);
     if (rc != DOPT_OK) return rc;
     if (!sc) return fail(DOPT_ERR_INVALID, "null scaler config");
-    if (!(sc->initial_scale > 0.0) || (sc->kind != DOPT_SCALER_CONSTANT && sc->kind != DOPT_SCALER_DYNAMIC))
-        return fail(DOPT_ERR_INVALID, "scaler: kind must be constant or dynamic and initial_scale > 0");
+    if (!usable_scale(sc->initial_scale) || (sc->kind != DOPT_SCALER_CONSTANT && sc->kind != DOPT_SCALER_DYNAMIC))
+        return fail(DOPT_ERR_INVALID, "scaler: kind must be constant or dynamic, and initial_scale finite and > 0 "
+                                      "with a finite nonzero fp32 reciprocal");
     if (sc->kind == DOPT_SCALER_DYNAMIC &&
-        (sc->hysteresis < 1 || sc->growth_interval < 1 || !(sc->growth_factor > 1.0) || !(sc->backoff_factor > 0.0) ||
-         !(sc->backoff_factor < 1.0) || !(sc->min_scale > 0.0)))
+        (sc->hysteresis < 1 || sc->growth_interval < 1 || !(sc->growth_factor > 1.0) || !std::isfinite(sc->growth_factor) ||
+         !(sc->backoff_factor > 0.0) || !(sc->backoff_factor < 1.0) || !usable_scale(sc->min_scale)))
         return fail(DOPT_ERR_INVALID, "dynamic scaler: bad hysteresis, interval or factors");
     for (const Buffer &B : L->buffers) {
         rc = hip_check(hipMemcpyAsync(ws_ptr(ws, B.ws_tiles), B.tiles.data(), B.tiles.size() * sizeof(TileDesc),
@@ -1716,7 +1726,9 @@ int dopt_state_scalars_get(const dopt_layout *L, const void *ws, hipStream_t str
 
 int dopt_state_scalars_set(const dopt_layout *L, void *ws, hipStream_t stream, const dopt_state_scalars *in) {
     if (!L || !ws || !in) return fail(DOPT_ERR_INVALID, "null layout, workspace or input");
-    if (!(in->loss_scale > 0.0) || in->step_count < 0) return fail(DOPT_ERR_INVALID, "bad scalar state");
+    if (!usable_scale(in->loss_scale) || in->step_count < 0)
+        return fail(DOPT_ERR_INVALID, "scalar state: loss_scale must be finite and > 0 with a finite nonzero fp32 "
+                                      "reciprocal, and step_count >= 0");
     DevState st;
     int rc = hip_check(hipMemcpyAsync(&st, ws_ptr(ws, kWsState), sizeof st, hipMemcpyDeviceToHost, stream),
                        "copy scalar state");

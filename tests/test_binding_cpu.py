@@ -181,3 +181,20 @@ def test_vmm_wrappers_report_hip_errors_as_dopt_errors():
         with pytest.raises(D.DoptError) as e:
             D.dopt_vmm_granularity(0)
         assert e.value.code == -4 and "hipMemGetAllocationGranularity" in str(e.value)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(initial_scale=float("inf")), dict(initial_scale=float("nan")), dict(initial_scale=1e-320),
+    dict(initial_scale=1e50), dict(dynamic=True, growth_factor=float("inf")), dict(dynamic=True, min_scale=1e-320),
+], ids=["inf", "nan", "reciprocal-inf", "reciprocal-zero", "growth-inf", "min-scale-reciprocal-inf"])
+def test_init_state_refuses_scales_without_a_usable_reciprocal(L, cfg):
+    """Every grad is unscaled by 1/scale in fp32: a scale that is not finite,
+    or whose fp32 reciprocal is infinite or zero, is refused before anything
+    touches a device (raw addresses)."""
+    _err(lambda: D.dopt_init_state(L, D.tensors(L, _bufs(L)), D.scaler_cfg(**cfg), 4096), "scale")
+
+
+@pytest.mark.parametrize("scale", [float("inf"), 0.0, 1e50, 1e-320])
+def test_scalar_set_refuses_scales_without_a_usable_reciprocal(L, scale):
+    _err(lambda: D.dopt_state_scalars_set(L, 4096, {"step_count": 3, "loss_scale": scale, "growth_tracker": 0,
+                                                    "hysteresis_tracker": 1}), "loss_scale", "finite")
