@@ -136,7 +136,8 @@ typedef struct dopt_layout dopt_layout;
  * owned by the library; free it with dopt_layout_free.
  * Errors: DOPT_ERR_INVALID (null pointers, n <= 0 or n > INT32_MAX,
  * numel <= 0, more than 2^52 elements over the list, bad dtype or hgroup,
- * N < 1, r outside [0, N)); DOPT_ERR_ASSERT; DOPT_ERR_NOMEM.
+ * N < 1, r outside [0, N), a flat buffer padded beyond 2^60 elements);
+ * DOPT_ERR_ASSERT; DOPT_ERR_NOMEM.
  */
 int dopt_build_ranges(const dopt_param_desc *params, int64_t n, const dopt_shard_cfg *cfg,
                       dopt_layout **out);

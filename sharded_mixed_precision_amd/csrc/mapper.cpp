@@ -30,6 +30,10 @@ static int64_t align_up(int64_t x, int64_t d) { return (x + d - 1) / d * d; }
 // The largest element count a param list may hold (far above any device
 // memory): every padded offset then stays far from the int64 limit.
 static constexpr int64_t kMaxListNumel = int64_t(1) << 52;
+// The largest padded buffer: each bucket's end is padded to a multiple of
+// up to about 2^47 elements (an odd dp_size near 2^31 with the high-busbw
+// padding), so many small buckets could otherwise carry offsets past int64.
+static constexpr int64_t kMaxBufferNumel = int64_t(1) << 60;
 
 static bool valid_dtype(int32_t d) { return d == DOPT_F32 || d == DOPT_BF16 || d == DOPT_F16; }
 
@@ -72,8 +76,12 @@ static int lay_out_buffer(dopt_layout &L, Buffer &B, int64_t bucket_size, bool b
         last_end = p.end;
         const bool full = bucket_size > 0 && (p.end - bucket_start) >= bucket_size;
         cursor = (full || p.newb) ? seal(p.end) : p.end;
+        if (cursor > kMaxBufferNumel)
+            return fail(DOPT_ERR_INVALID, "the padded buffer holds more than 2^60 elements");
     }
     if (open > 0) seal(last_end);
+    if (bucket_start > kMaxBufferNumel)
+        return fail(DOPT_ERR_INVALID, "the padded buffer holds more than 2^60 elements");
 
     B.numel = bucket_start;
     B.unpadded = 0;

@@ -154,6 +154,13 @@ def test_mapper_errors():
         with pytest.raises(d.DoptError) as e:
             d.dopt_build_ranges(big, 8, 0)
         assert e.value.code == -1
+    # padding alone past the 64-bit range: 9000 one-param buckets (bucket_size
+    # 1), each padded to a multiple of (2^31 - 1) * 2^16 elements (an odd
+    # dp_size with the high-busbw padding), is 1.27e18 > 2^60 padded elements
+    many = [ParamSpec(f"p{i}", 128, "bf16", "bf16") for i in range(9000)]
+    with pytest.raises(d.DoptError) as e:
+        d.dopt_build_ranges(many, (1 << 31) - 1, 5, 1, 1)
+    assert e.value.code == -1 and "2^60" in str(e.value)
     L = d.dopt_build_ranges(ok, 2, 1)
     with pytest.raises(d.DoptError) as e:
         L.buffer(3)
