@@ -53,15 +53,15 @@ REGION_ELEMS = 1 << 27  # arena elements per placement region
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 106,582.25 KiB * 2.0 + WRITE_SIZE 213,544.89 KiB * 1.0, averaged over 523 dispatches
+    # FETCH_SIZE 106,578.74 KiB * 2.0 + WRITE_SIZE 213,612.00 KiB * 1.0, averaged over 523 dispatches
     # (profiles/k_apply_gpt2-small_kernel_trace.md)
-    "gpt2-small": {"src": "3e81492db41c2e04", "bytes_per_launch": 436950416},
-    # FETCH_SIZE 46,269,107.44 KiB * 2.0 + WRITE_SIZE 92,127,730.79 KiB * 1.0, averaged over the 37
+    "gpt2-small": {"src": "cbad5d318d97ee84", "bytes_per_launch": 437011936},
+    # FETCH_SIZE 46,269,107.64 KiB * 2.0 + WRITE_SIZE 92,127,615.99 KiB * 1.0, averaged over the 37
     # full-window dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
-    "dense-7b": {"src": "3e81492db41c2e04", "bytes_per_launch": 189097928375},
-    # k_apply_bnd: FETCH_SIZE 7,569,698.34 KiB * 2.0 + WRITE_SIZE 15,072,172.86 KiB * 1.0, averaged over 37
+    "dense-7b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 189097811214},
+    # k_apply_bnd: FETCH_SIZE 7,569,698.09 KiB * 2.0 + WRITE_SIZE 15,072,212.25 KiB * 1.0, averaged over 37
     # dispatches (profiles/k_apply_llama3-70b_kernel_trace.md)
-    "llama3-70b": {"src": "3e81492db41c2e04", "bytes_per_launch": 30936647216},
+    "llama3-70b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 30936687031},
 }
 
 
