@@ -62,6 +62,10 @@ MEASURED_TRAFFIC = {
     # k_apply_bnd: FETCH_SIZE 7,569,698.09 KiB * 2.0 + WRITE_SIZE 15,072,212.25 KiB * 1.0, averaged over 37
     # dispatches (profiles/k_apply_llama3-70b_kernel_trace.md)
     "llama3-70b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 30936687031},
+    # both buffers' launches of one step (the bf16-param / fp32-grad window and the fp32 norms):
+    # FETCH_SIZE 7,872,473.16 + 311.88 KiB * 2.0 + WRITE_SIZE 13,723,536.26 + 390.00 KiB * 1.0, averaged
+    # over 37 dispatches each (profiles/k_apply_llama3-8b_kernel_trace.md)
+    "llama3-8b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 30176764250},
 }
 
 
