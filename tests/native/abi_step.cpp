@@ -1,11 +1,15 @@
 // A native consumer of the C ABI in include/dopt.h: no Python, no PyTorch.
 // It builds a layout, allocates every device array with hipMalloc, runs the
-// steps of an input file through dopt_init_state / dopt_step on its own HIP
-// stream, and writes the stats and the final arenas to an output file for
-// the test to compare with the oracle.
+// steps of an input file on its own HIP stream, and writes the stats and the
+// final arenas to an output file for the test to compare with the oracle.
 //
 //   abi_step layout <in.bin>            print the layout's arena sizes (host only, no GPU)
-//   abi_step run <in.bin> <out.bin>     run the steps on the GPU
+//   abi_step run <in.bin> <out.bin>     dopt_init_state, then dopt_step per step
+//   abi_step reduce <in.bin> <out.bin>  dopt_init_state, then per step the fused
+//                                       reduce of the received chunks with the
+//                                       finalize (dopt_reduce_prepare), dopt_step_apply
+//                                       and dopt_read_stats; after the steps the
+//                                       state export and the scalar state
 //
 // in.bin (little-endian):
 //   int32 magic 0x444f5054, n_params, dp_size, dp_rank, steps, n_hgroups
@@ -14,13 +18,19 @@
 //   n_hgroups x {double lr, beta1, beta2, eps, weight_decay}
 //   n_params  x {int64 numel; int32 param_dtype, grad_dtype, hgroup}
 //   per buffer: int64 arena_numel (must equal the layout's)
+//   reduce mode only: int32 wire_dtype; float scale
 //   per buffer: the initial param arena (arena_numel x param dtype)
-//   per step, per buffer: the grad arena (arena_numel x grad dtype)
+//   per step, per buffer: run: the grad arena (arena_numel x grad dtype);
+//                         reduce: dp_size chunks back to back (dp_size x arena_numel x wire dtype)
 // out.bin:
 //   per step: dopt_stats as the ABI defines it
 //   per buffer: master (16-bit params only), exp_avg, exp_avg_sq (fp32 arenas), param arena
+//   reduce mode only, then: per buffer the grad arena (the last step's reduced grads);
+//     int64 state_numel; the exported master, exp_avg, exp_avg_sq (state_numel fp32 each);
+//     dopt_state_scalars as the ABI defines it
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -121,7 +131,7 @@ struct DevBuf {
 }  // namespace
 
 int main(int argc, char **argv) {
-    if (argc < 3) die("usage: abi_step layout <in.bin> | abi_step run <in.bin> <out.bin>");
+    if (argc < 3) die("usage: abi_step layout <in.bin> | abi_step run|reduce <in.bin> <out.bin>");
     const std::string mode = argv[1];
     FILE *f = std::fopen(argv[2], "rb");
     if (!f) die(std::string("cannot open ") + argv[2]);
@@ -140,9 +150,17 @@ int main(int argc, char **argv) {
         dopt_layout_free(L);
         return 0;
     }
-    if (mode != "run" || argc < 4) die("usage: abi_step run <in.bin> <out.bin>");
+    if ((mode != "run" && mode != "reduce") || argc < 4) die("usage: abi_step run|reduce <in.bin> <out.bin>");
+    const bool reduce = mode == "reduce";
     for (int32_t k = 0; k < nb; ++k)
         if (rd.get<int64_t>() != bufs[k].info.arena_numel) die("arena size in the input differs from the layout's");
+    int32_t wire = DOPT_BF16;
+    float scale = 1.0f;
+    if (reduce) {
+        wire = rd.get<int32_t>();
+        scale = rd.get<float>();
+        if (wire != DOPT_F32 && wire != DOPT_BF16 && wire != DOPT_F16) die("bad wire dtype");
+    }
 
     hipStream_t stream;
     hk(hipStreamCreate(&stream), "hipStreamCreate");
@@ -162,6 +180,12 @@ int main(int argc, char **argv) {
     }
     void *ws = nullptr;
     hk(hipMalloc(&ws, static_cast<size_t>(dopt_workspace_bytes(L))), "hipMalloc workspace");
+    // reduce mode: one receive buffer per flat buffer, the dp_size chunks back to back
+    std::vector<void *> chunks(static_cast<size_t>(nb), nullptr);
+    if (reduce)
+        for (int32_t k = 0; k < nb; ++k)
+            hk(hipMalloc(&chunks[k], static_cast<size_t>(in.N * bufs[k].info.arena_numel * elem_bytes(wire))),
+               "hipMalloc chunks");
     dopt_scaler_cfg sc;
     std::memset(&sc, 0, sizeof sc);
     sc.kind = DOPT_SCALER_CONSTANT;
@@ -173,13 +197,24 @@ int main(int argc, char **argv) {
     for (int32_t s = 0; s < in.steps; ++s) {
         for (int32_t k = 0; k < nb; ++k) {
             const int64_t n = bufs[k].info.arena_numel;
-            std::vector<char> host(static_cast<size_t>(n * elem_bytes(bufs[k].info.grad_dtype)));
+            const int64_t bytes = reduce ? in.N * n * elem_bytes(wire) : n * elem_bytes(bufs[k].info.grad_dtype);
+            std::vector<char> host(static_cast<size_t>(bytes));
             rd.bytes(host.data(), host.size());
-            hk(hipMemcpyAsync(bufs[k].grad, host.data(), host.size(), hipMemcpyHostToDevice, stream), "copy grad");
-            hk(hipStreamSynchronize(stream), "synchronize after the grad copy");
+            hk(hipMemcpyAsync(reduce ? chunks[k] : bufs[k].grad, host.data(), host.size(), hipMemcpyHostToDevice,
+                              stream),
+               "copy grad or chunks");
+            hk(hipStreamSynchronize(stream), "synchronize after the input copy");
         }
         dopt_stats st;
-        ck(dopt_step(L, t.data(), in.hp.data(), in.n_hgroups, in.max_norm, ws, stream, &st), "dopt_step");
+        if (reduce) {
+            ck(dopt_reduce_prepare(L, t.data(), chunks.data(), nullptr, wire, in.N, scale, in.hp.data(), in.n_hgroups,
+                                   in.max_norm, ws, stream),
+               "dopt_reduce_prepare");
+            ck(dopt_step_apply(L, t.data(), ws, stream), "dopt_step_apply");
+            ck(dopt_read_stats(L, ws, stream, &st), "dopt_read_stats");
+        } else {
+            ck(dopt_step(L, t.data(), in.hp.data(), in.n_hgroups, in.max_norm, ws, stream, &st), "dopt_step");
+        }
         std::fwrite(&st, sizeof st, 1, o);
     }
     for (int32_t k = 0; k < nb; ++k) {
@@ -197,6 +232,31 @@ int main(int argc, char **argv) {
         const size_t pb = static_cast<size_t>(n * elem_bytes(b.info.param_dtype));
         hk(hipMemcpy(host.data(), b.param, pb, hipMemcpyDeviceToHost), "copy param");
         std::fwrite(host.data(), 1, pb, o);
+    }
+    if (reduce) {
+        for (int32_t k = 0; k < nb; ++k) {
+            const int64_t gb = bufs[k].info.arena_numel * elem_bytes(bufs[k].info.grad_dtype);
+            std::vector<char> host(static_cast<size_t>(gb));
+            hk(hipMemcpy(host.data(), bufs[k].grad, gb, hipMemcpyDeviceToHost), "copy reduced grad");
+            std::fwrite(host.data(), 1, host.size(), o);
+        }
+        const int64_t sn = dopt_layout_state_numel(L);
+        std::fwrite(&sn, sizeof sn, 1, o);
+        float *ex[3] = {nullptr, nullptr, nullptr};
+        for (float *&e : ex) hk(hipMalloc(reinterpret_cast<void **>(&e), static_cast<size_t>(std::max<int64_t>(sn, 1) * 4)),
+                                "hipMalloc export");
+        ck(dopt_state_export(L, t.data(), ex[0], ex[1], ex[2], ws, stream), "dopt_state_export");
+        hk(hipStreamSynchronize(stream), "synchronize after the export");
+        std::vector<float> host(static_cast<size_t>(sn));
+        for (float *e : ex) {
+            hk(hipMemcpy(host.data(), e, static_cast<size_t>(sn * 4), hipMemcpyDeviceToHost), "copy export");
+            std::fwrite(host.data(), 4, host.size(), o);
+            hk(hipFree(e), "hipFree");
+        }
+        dopt_state_scalars sc_out;
+        ck(dopt_state_scalars_get(L, ws, stream, &sc_out), "dopt_state_scalars_get");
+        std::fwrite(&sc_out, sizeof sc_out, 1, o);
+        for (void *c : chunks) hk(hipFree(c), "hipFree");
     }
     std::fclose(o);
     std::fclose(f);

@@ -1,11 +1,14 @@
 """The C ABI driven by a native C++ program (tests/native/abi_step), with no
 Python or PyTorch in the process that calls it: every device array is
-hipMalloc'd by the program and the steps run on its own HIP stream.
+hipMalloc'd by the program and the steps run on its own HIP stream (in one
+mode through dopt_step, in the other through the fused reduce, the split
+step, the state export and the scalar state).
 
 The CPU test runs the program's layout mode (host-side mapper only) and
 checks it against the Python binding's view of the same layout.  The GPU
-test feeds it seeded synthetic params and grads through a file, runs the
-steps, and compares the stats and every shard element of the final state
+tests feed it seeded synthetic params and grads (or received grad chunks)
+through a file, run the steps, and compare the stats and every shard element
+of the final state (and the reduced grads, the export and the scalar state)
 with the oracle on the same inputs, to the bars of the other parity tests.
 """
 import ctypes
@@ -16,10 +19,11 @@ import subprocess
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from synth.models import ParamSpec
 from tests import gpu_harness as H
-from tests.oracle_harness import OracleRun, to_bits
+from tests.oracle_harness import OracleRun, oracle_export, to_bits
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 EXE = os.path.join(ROOT, "tests", "native", "abi_step")
@@ -106,4 +110,72 @@ def test_native_step_matches_oracle(tmp_path):
         got = np.frombuffer(data, pdt, n, off)
         off += ES[b["pd"]] * n
         H.check_param(f"buffer {k} param", got[valid].copy(), b["param"][valid].copy(), b["pd"])
+    assert off == len(data)
+
+
+@pytest.mark.gpu
+def test_native_reduce_export_matches_oracle(tmp_path):
+    """The reduce mode: per step the dp_size received bf16 chunks of each
+    buffer go through dopt_reduce_prepare (fp32-accumulating reduce, scaled by
+    1/dp_size, pass 1, finalize), dopt_step_apply and dopt_read_stats; then the
+    state export and the scalar state.  Against the oracle's reduce and step
+    on the same chunks: the stats, every reduced window slot and every shard
+    element bit for bit, the export arrays bit for bit, and the step count."""
+    D, L = _binding_layout()
+    nb = L.num_buffers
+    arena = [L.buffer(k)["arena_numel"] for k in range(nb)]
+    run = OracleRun(PARAMS, N, R, BUCKET, arena_numel=arena)
+    scale = 1.0 / N
+    blob = [_header(STEPS), struct.pack(f"<{nb}q", *arena), struct.pack("<if", DT["bf16"], scale)]
+    for k, b in enumerate(run.bufs):
+        b["param"][:] = to_bits(synth.fill_normal(b["pd"], b["n"], 0, synth.weight_stream(k), 0, 0.02))
+        blob.append(b["param"].tobytes())
+    run.init_state()
+    ref_stats = []
+    for s in range(1, STEPS + 1):
+        for k, b in enumerate(run.bufs):
+            ch = synth.fill_normal("bf16", N * b["n"], 0, synth.chunk_stream(k), s, 1e-2)
+            blob.append(to_bits(ch).tobytes())
+            oracle.lib().or_reduce_chunks(run.L.handle, k, ch.data_ptr(), oracle.DTYPES["bf16"], N, b["n"],
+                                          ctypes.c_float(scale), 0, b["n"], b["grad"].ctypes.data)
+        ref_stats.append(run.step(HPS, MAX_NORM))
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    fin.write_bytes(b"".join(blob))
+    out = subprocess.run([_exe(), "reduce", str(fin), str(fout)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    data = fout.read_bytes()
+    sz = ctypes.sizeof(D.dopt_stats)
+    off = 0
+    for s, ref in enumerate(ref_stats):
+        st = D.dopt_stats.from_buffer_copy(data[off:off + sz]).as_dict()
+        off += sz
+        H.check_stats(st, ref, s + 1)
+    for k, b in enumerate(run.bufs):
+        n = b["n"]
+        valid = run.valid(k)
+        for key in (["master"] if b["pd"] != "f32" else []) + ["m", "v"]:
+            got = np.frombuffer(data, np.float32, n, off)
+            off += 4 * n
+            H.check_f32(f"buffer {k} {key}", got[valid], b[key][valid])
+        pdt = np.float32 if b["pd"] == "f32" else np.uint16
+        got = np.frombuffer(data, pdt, n, off)
+        off += ES[b["pd"]] * n
+        H.check_param(f"buffer {k} param", got[valid].copy(), b["param"][valid].copy(), b["pd"])
+    for k, b in enumerate(run.bufs):  # the last step's reduced grads, every window slot
+        gdt = np.float32 if b["gd"] == "f32" else np.uint16
+        got = np.frombuffer(data, gdt, b["n"], off)
+        off += ES[b["gd"]] * b["n"]
+        w = run.L.buffer(k)["window_numel"]  # the arena's tail past the window is tile padding
+        assert np.array_equal(got[:w].view(np.uint8), b["grad"][:w].view(np.uint8)), f"buffer {k} reduced grad"
+    sn = struct.unpack_from("<q", data, off)[0]
+    off += 8
+    assert sn == L.state_numel
+    ref_ex = oracle_export(run)
+    for key, ref in zip(("master", "exp_avg", "exp_avg_sq"), ref_ex):
+        got = np.frombuffer(data, np.float32, sn, off)
+        off += 4 * sn
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"export {key}"
+    sc = struct.unpack_from("<qdqq", data, off)
+    off += struct.calcsize("<qdqq")
+    assert sc[0] == STEPS and sc[1] == 1.0, sc
     assert off == len(data)
