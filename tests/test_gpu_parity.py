@@ -6,8 +6,9 @@ oracle computing the exact per-step statistics over every shard element and
 the trajectories of about a million sampled elements per buffer (plus every
 segment's first and last element).  Edge cases: windows that start at odd
 offsets, empty windows, mixed dtypes and hyper-groups, lone-param buckets,
-bus-bandwidth padding, all-zero grads, NaN / -inf overflow, clipping on and
-off, the three-call split API, and run-to-run determinism.
+bus-bandwidth padding, all-zero grads, NaN / -inf overflow, the dynamic loss
+scaler's growth, hysteresis, backoff and floor, clipping on and off, the
+three-call split API, and run-to-run determinism.
 """
 import math
 
@@ -15,9 +16,11 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from synth.models import ParamSpec
 from tests import gpu_harness as H
+from tests.oracle_harness import OracleRun, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +145,62 @@ def test_overflow_skips_step(bad):
     params = [ParamSpec("a", 40000, "f16", "f16"), ParamSpec("b", 1000, "f16", "f16")]
     H.run_full(H.Case("overflow", params, 2, 0, steps=4, dynamic=True, initial_scale=1024.0, inf_step=2,
                       inf_value=bad, grad_sigma=1e-3))
+
+
+def test_dynamic_scaler_growth_hysteresis_backoff_and_floor():
+    """The dynamic loss scaler through each of its rules, with a growth
+    interval of 2 and a hysteresis of 2: growth after clean steps, the first
+    overflow of a run kept at the same scale, backoff from the second on, the
+    minimum scale as a floor, and the hysteresis restored by a growth.  13
+    steps, overflows planted at steps 3, 4 and 7 to 11, each step's grads
+    drawn at the scale the step carries.  Every step: the stats, the scalar
+    state (scale, growth and hysteresis trackers, step count) and every shard
+    element against the oracle."""
+    params = [ParamSpec("a", 5000, "bf16", "bf16"), ParamSpec("h", 3000, "f16", "f16")]
+    rules = dict(growth_factor=2.0, backoff_factor=0.5, growth_interval=2, hysteresis=2, min_scale=4.0)
+    case = H.Case("scaler-rules", params, 2, 1, 0, steps=13, dynamic=True, initial_scale=16.0)
+    dev = H.DeviceRun(case)
+    D = dev.D
+    arena = [dev.L.buffer(k)["arena_numel"] for k in range(dev.L.num_buffers)]
+    orc = OracleRun(params, 2, 1, 0, arena_numel=arena)
+    orc.scaler = oracle.make_scaler(True, 16.0, **rules)
+    for k, b in enumerate(orc.bufs):
+        t = H.host_weights(case, k, b["pd"], b["n"])
+        b["param"][:] = to_bits(t)
+        dev.A.bufs[k]["param"].copy_(t)
+    D.dopt_init_state(dev.L, dev.A.bufs, D.scaler_cfg(True, 16.0, **rules), dev.A.workspace, dev.stream)
+    orc.init_state()
+    masks = [orc.valid(k) for k in range(orc.nb)]
+    scales = []
+    for s in range(1, case.steps + 1):
+        carried = orc.scaler.scale
+        grads = []
+        for k, b in enumerate(orc.bufs):
+            g = synth.fill_normal(b["gd"], b["n"], 0, synth.grad_stream(k), s, 1e-2, scale=carried)
+            if s in (3, 4, 7, 8, 9, 10, 11) and k == s % 2:
+                owned = np.flatnonzero(masks[k])
+                g[int(owned[(37 * s) % owned.size])] = math.inf
+            b["grad"][:] = to_bits(g)
+            grads.append(g)
+        ref = orc.step(case.hparams, case.max_norm)
+        got = dev.step(grads)
+        H.check_stats(got, ref, s)
+        sc = D.dopt_state_scalars_get(dev.L, dev.A.workspace, dev.stream)
+        assert sc == {"step_count": orc.t, "loss_scale": orc.scaler.scale,
+                      "growth_tracker": orc.scaler.growth_tracker,
+                      "hysteresis_tracker": orc.scaler.hysteresis_tracker}, (s, sc)
+        for k, b in enumerate(orc.bufs):
+            m = masks[k]
+            H.check_f32(f"step {s} master[{k}]", dev.host(k, "master")[m], b["master"][m])
+            H.check_f32(f"step {s} m[{k}]", dev.host(k, "exp_avg")[m], b["m"][m])
+            H.check_f32(f"step {s} v[{k}]", dev.host(k, "exp_avg_sq")[m], b["v"][m])
+            H.check_param(f"step {s} param[{k}]", dev.host(k, "param")[m], b["param"][m], b["pd"])
+        scales.append((carried, bool(ref.skipped), orc.scaler.scale))
+    # every rule was taken: a growth, an overflow kept at its scale, a backoff, and the floor
+    assert any(not sk and after > before for before, sk, after in scales), scales
+    assert any(sk and after == before for before, sk, after in scales), scales
+    assert any(sk and after < before for before, sk, after in scales), scales
+    assert any(sk and before == rules["min_scale"] and after == before for before, sk, after in scales), scales
 
 
 def test_clip_off_and_clip_active():
