@@ -68,7 +68,8 @@ def test_reduce_padded_chunk_stride_large_window():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("n,wire", [(1, "bf16"), (3, "bf16"), (3, "f32")], ids=["1-bf16", "3-bf16", "3-f32"])
+@pytest.mark.parametrize("n,wire", [(1, "bf16"), (3, "bf16"), (3, "f32"), (3, "f16")],
+                         ids=["1-bf16", "3-bf16", "3-f32", "3-f16"])
 def test_reduce_large_window_odd_chunk_counts(n, wire):
     """A window past the one-tile-per-workgroup grid (the large-window reduce,
     which issues its chunk loads two at a time) reduced from an odd number of
