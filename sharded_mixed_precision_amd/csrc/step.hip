@@ -242,6 +242,23 @@ __device__ __forceinline__ void store8f(float *base, int64_t i, const float (&x)
     *reinterpret_cast<f32x4 *>(base + i + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// Elem<GD>::store8 with the nontemporal hint (16-byte stores).
+template <int GD>
+__device__ __forceinline__ void store8_nt(void *base, int64_t i, const float (&x)[kVec]) {
+    if constexpr (GD == DOPT_F32) {
+        float *b = static_cast<float *>(base) + i;
+        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(b));
+        __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4 *>(b + 4));
+    } else {
+        u32x4 u;
+        u[0] = Elem<GD>::bits(x[0]) | (Elem<GD>::bits(x[1]) << 16);
+        u[1] = Elem<GD>::bits(x[2]) | (Elem<GD>::bits(x[3]) << 16);
+        u[2] = Elem<GD>::bits(x[4]) | (Elem<GD>::bits(x[5]) << 16);
+        u[3] = Elem<GD>::bits(x[6]) | (Elem<GD>::bits(x[7]) << 16);
+        __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + i));
+    }
+}
+
 __device__ __forceinline__ void bload8f(__amdgpu_buffer_rsrc_t r, int32_t lane, float (&x)[kVec]) {
     const u32x4 a = bld16(r, lane * 32);
     const u32x4 b = bld16(r, lane * 32 + 16);
@@ -551,7 +568,11 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 // BATCH = kReduceBatchLarge.  On MI355X with the whole chip busy, 2 loads
 // per thread read 64 bf16 chunks 6% faster than 1 and 8 chunks with an fp32
 // grad write as fast; 4, or 2 on twice the workgroups, put so many requests
-// in flight that the mixed read and write streams slowed down.
+// in flight that the mixed read and write streams slowed down.  NT_GRAD
+// stores the reduced grads with the nontemporal hint: large windows, whose
+// grads far exceed the last-level cache, reduced 2-4% faster that way (64
+// bf16 chunks 6.15-6.17 against 5.93-5.98 TB/s); small ones keep ordinary
+// stores, so that pass 2 can still find their grads in the cache.
 constexpr int kReduceBatch = 8;
 constexpr int kReduceBatchLarge = 2;
 
@@ -564,7 +585,7 @@ __device__ __forceinline__ float stored_value<DOPT_BF16>(float x) { return __uin
 template <>
 __device__ __forceinline__ float stored_value<DOPT_F16>(float x) { return Elem<DOPT_F16>::up(Elem<DOPT_F16>::bits(x)); }
 
-template <int WD, int GD, int BATCH>
+template <int WD, int GD, int BATCH, bool NT_GRAD>
 __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict__ chunks, int64_t stride,
                                                         int32_t n_chunks, float scale, void *__restrict__ grad,
                                                         const TileDesc *__restrict__ tiles,
@@ -604,7 +625,10 @@ __global__ void __launch_bounds__(kBlock) k_reduce_stats(const void *__restrict_
         }
 #pragma unroll
         for (int j = 0; j < kVec; ++j) s[j] = s[j] * scale;
-        Elem<GD>::store8(grad, i0, s);
+        if constexpr (NT_GRAD)
+            store8_nt<GD>(grad, i0, s);
+        else
+            Elem<GD>::store8(grad, i0, s);
         const int32_t cnt = td.seg_count & kTileCountMask;
         if (cnt == 0) continue;
         const bool full = (td.seg_count & kTileFull) != 0;
@@ -1072,7 +1096,11 @@ k_apply_bnd(const void *__restrict__ grad, void *__restrict__ param, float *__re
 // Every shard element e of the arena corresponds to export slot
 // xoff(seg) + (e - seg.start).  Lane l of a workgroup takes elements
 // tile*kTile + j*kBlock + l (j = 0..7), so a wave touches 64 consecutive
-// arena slots and, within one segment, 64 consecutive export slots.
+// arena slots and, within one segment, 64 consecutive export slots.  The
+// fp32 stores carry the nontemporal hint: nothing reads an export soon, and an
+// import's arrays are next read by a pass that streams them from HBM.  On
+// MI355X the hint took the Llama-3 ranks' import from 5.83-5.85 to 6.02-6.07
+// TB/s (70B) and from 6.17-6.25 to 6.30-6.37 TB/s (8B), the export 1-3%.
 template <int PD, bool IMPORT>
 __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param, float *__restrict__ master,
                                                       float *__restrict__ m, float *__restrict__ v,
@@ -1103,14 +1131,14 @@ __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param,
             for (int j = 0; j < kVec; ++j) {
                 const int64_t e = e0 + int64_t(j) * kBlock;
                 if (IMPORT) {
-                    pm[e] = a[j];
-                    m[e] = b[j];
-                    v[e] = c[j];
+                    __builtin_nontemporal_store(a[j], pm + e);
+                    __builtin_nontemporal_store(b[j], m + e);
+                    __builtin_nontemporal_store(c[j], v + e);
                     if (PD != DOPT_F32) Elem<PD>::store1(param, e, a[j]);
                 } else {
-                    xm[e + dx] = a[j];
-                    xa[e + dx] = b[j];
-                    xv[e + dx] = c[j];
+                    __builtin_nontemporal_store(a[j], xm + e + dx);
+                    __builtin_nontemporal_store(b[j], xa + e + dx);
+                    __builtin_nontemporal_store(c[j], xv + e + dx);
                 }
             }
             continue;
@@ -1153,14 +1181,14 @@ __global__ void __launch_bounds__(kBlock) k_state_copy(void *__restrict__ param,
             if ((own >> j) & 1u) {
                 const int64_t e = e0 + int64_t(j) * kBlock;
                 if (IMPORT) {
-                    pm[e] = a[j];
-                    m[e] = b[j];
-                    v[e] = c[j];
+                    __builtin_nontemporal_store(a[j], pm + e);
+                    __builtin_nontemporal_store(b[j], m + e);
+                    __builtin_nontemporal_store(c[j], v + e);
                     if (PD != DOPT_F32) Elem<PD>::store1(param, e, a[j]);
                 } else {
-                    xm[e + dx[j]] = a[j];
-                    xa[e + dx[j]] = b[j];
-                    xv[e + dx[j]] = c[j];
+                    __builtin_nontemporal_store(a[j], xm + e + dx[j]);
+                    __builtin_nontemporal_store(b[j], xa + e + dx[j]);
+                    __builtin_nontemporal_store(c[j], xv + e + dx[j]);
                 }
             }
         }
@@ -1335,7 +1363,8 @@ static int launch_stats(const dopt_layout *L, const dopt_buffer_tensors *bufs, v
 
 // One launch of the fused reduce over tiles [t0, t1) of a buffer; small
 // windows (one launch, one tile per workgroup) keep kReduceBatch chunk loads
-// in flight per thread, large ones kReduceBatchLarge.
+// in flight per thread, large ones kReduceBatchLarge and store their grads
+// with the nontemporal hint.
 struct ReduceLaunch {
     dim3 grid;
     const void *chunks;
@@ -1354,11 +1383,11 @@ struct ReduceLaunch {
 template <int WD, int GD>
 static void launch_reduce_dt(const ReduceLaunch &r, hipStream_t s) {
     if (r.small)
-        k_reduce_stats<WD, GD, kReduceBatch><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad,
-                                                                       r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
+        k_reduce_stats<WD, GD, kReduceBatch, false><<<r.grid, kBlock, 0, s>>>(
+            r.chunks, r.stride, r.n, r.scale, r.grad, r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
     else
-        k_reduce_stats<WD, GD, kReduceBatchLarge><<<r.grid, kBlock, 0, s>>>(r.chunks, r.stride, r.n, r.scale, r.grad,
-                                                                            r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
+        k_reduce_stats<WD, GD, kReduceBatchLarge, true><<<r.grid, kBlock, 0, s>>>(
+            r.chunks, r.stride, r.n, r.scale, r.grad, r.tiles, r.segs, r.t0, r.t1, r.st, r.out);
 }
 
 template <int WD>
