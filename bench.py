@@ -53,19 +53,19 @@ REGION_ELEMS = 1 << 27  # arena elements per placement region
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 106,578.74 KiB * 2.0 + WRITE_SIZE 213,612.00 KiB * 1.0, averaged over 523 dispatches
+    # FETCH_SIZE 106,584.29 KiB * 2.0 + WRITE_SIZE 213,620.45 KiB * 1.0, averaged over 523 dispatches
     # (profiles/k_apply_gpt2-small_kernel_trace.md)
-    "gpt2-small": {"src": "cbad5d318d97ee84", "bytes_per_launch": 437011936},
-    # FETCH_SIZE 46,269,107.64 KiB * 2.0 + WRITE_SIZE 92,127,615.99 KiB * 1.0, averaged over the 37
+    "gpt2-small": {"src": "98df89ac165834d2", "bytes_per_launch": 437031966},
+    # FETCH_SIZE 46,269,092.75 KiB * 2.0 + WRITE_SIZE 92,127,541.74 KiB * 1.0, averaged over the 37
     # full-window dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
-    "dense-7b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 189097811214},
-    # k_apply_bnd: FETCH_SIZE 7,569,698.09 KiB * 2.0 + WRITE_SIZE 15,072,212.25 KiB * 1.0, averaged over 37
+    "dense-7b": {"src": "98df89ac165834d2", "bytes_per_launch": 189097704704},
+    # k_apply_bnd: FETCH_SIZE 7,569,698.12 KiB * 2.0 + WRITE_SIZE 15,072,114.70 KiB * 1.0, averaged over 37
     # dispatches (profiles/k_apply_llama3-70b_kernel_trace.md)
-    "llama3-70b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 30936687031},
+    "llama3-70b": {"src": "98df89ac165834d2", "bytes_per_launch": 30936587209},
     # both buffers' launches of one step (the bf16-param / fp32-grad window and the fp32 norms):
-    # FETCH_SIZE 7,872,473.16 + 311.88 KiB * 2.0 + WRITE_SIZE 13,723,536.26 + 390.00 KiB * 1.0, averaged
+    # FETCH_SIZE 7,872,472.42 + 311.88 KiB * 2.0 + WRITE_SIZE 13,723,597.60 + 390.00 KiB * 1.0, averaged
     # over 37 dispatches each (profiles/k_apply_llama3-8b_kernel_trace.md)
-    "llama3-8b": {"src": "cbad5d318d97ee84", "bytes_per_launch": 30176764250},
+    "llama3-8b": {"src": "98df89ac165834d2", "bytes_per_launch": 30176825531},
 }
 
 
