@@ -242,13 +242,31 @@ __device__ __forceinline__ void store8f(float *base, int64_t i, const float (&x)
     *reinterpret_cast<f32x4 *>(base + i + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-// Elem<GD>::store8 with the nontemporal hint (16-byte stores).
+// Elem<GD>::store8 with the nontemporal hint (16-byte stores), called by all
+// 64 lanes of a wave together, lane l holding elements i .. i+7 with
+// i = (the wave's first element) + 8l.  For fp32 each store instruction
+// covers one contiguous KiB: lane l writes elements 4l .. 4l+3 and
+// 256+4l .. 256+4l+3 of the wave's 512, taken from the lanes that hold them
+// (l>>1 and 32 + (l>>1)).  Two stores of a lane's own halves would leave
+// every other 16 bytes of each instruction's lines unwritten, and streaming
+// stores of such partial lines raised the reduce's write traffic by 11%.
 template <int GD>
 __device__ __forceinline__ void store8_nt(void *base, int64_t i, const float (&x)[kVec]) {
     if constexpr (GD == DOPT_F32) {
-        float *b = static_cast<float *>(base) + i;
-        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(b));
-        __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4 *>(b + 4));
+        const int l = static_cast<int>(threadIdx.x & 63);
+        const int s0 = l >> 1, s1 = 32 + (l >> 1);
+        const bool odd = (l & 1) != 0;
+        f32x4 a, c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo0 = __shfl(x[q], s0, 64), hi0 = __shfl(x[4 + q], s0, 64);
+            const float lo1 = __shfl(x[q], s1, 64), hi1 = __shfl(x[4 + q], s1, 64);
+            a[q] = odd ? hi0 : lo0;
+            c[q] = odd ? hi1 : lo1;
+        }
+        float *w = static_cast<float *>(base) + (i - int64_t(l) * kVec);
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(w + 4 * l));
+        __builtin_nontemporal_store(c, reinterpret_cast<f32x4 *>(w + 256 + 4 * l));
     } else {
         u32x4 u;
         u[0] = Elem<GD>::bits(x[0]) | (Elem<GD>::bits(x[1]) << 16);
@@ -571,8 +589,9 @@ __global__ void __launch_bounds__(kBlock) k_stats(const void *__restrict__ grad,
 // in flight that the mixed read and write streams slowed down.  NT_GRAD
 // stores the reduced grads with the nontemporal hint: large windows, whose
 // grads far exceed the last-level cache, reduced 2-4% faster that way (64
-// bf16 chunks 6.15-6.17 against 5.93-5.98 TB/s); small ones keep ordinary
-// stores, so that pass 2 can still find their grads in the cache.
+// bf16 chunks 6.15-6.17 against 5.93-5.98 TB/s, 8 chunks into fp32 grads
+// 5.79-5.83 against 5.58-5.61 with ordinary stores); small ones keep
+// ordinary stores, so that pass 2 can still find their grads in the cache.
 constexpr int kReduceBatch = 8;
 constexpr int kReduceBatchLarge = 2;
 
