@@ -53,19 +53,19 @@ REGION_ELEMS = 1 << 27  # arena elements per placement region
 # bytes_per_launch = FETCH_SIZE * 2.0 + WRITE_SIZE * 1.0 (KiB -> B), the scale
 # factors read off a 1 GiB fp32 copy.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 106,584.29 KiB * 2.0 + WRITE_SIZE 213,620.45 KiB * 1.0, averaged over 523 dispatches
+    # FETCH_SIZE 106,556.68 KiB * 2.0 + WRITE_SIZE 213,569.33 KiB * 1.0, averaged over 523 dispatches
     # (profiles/k_apply_gpt2-small_kernel_trace.md)
-    "gpt2-small": {"src": "98df89ac165834d2", "bytes_per_launch": 437031966},
-    # FETCH_SIZE 46,269,092.75 KiB * 2.0 + WRITE_SIZE 92,127,541.74 KiB * 1.0, averaged over the 37
+    "gpt2-small": {"src": "53d67aba3946e0d0", "bytes_per_launch": 436923071},
+    # FETCH_SIZE 46,269,131.90 KiB * 2.0 + WRITE_SIZE 92,127,420.10 KiB * 1.0, averaged over the 37
     # full-window dispatches that were not overflow-skipped (profiles/k_apply_dense-7b_kernel_trace.md)
-    "dense-7b": {"src": "98df89ac165834d2", "bytes_per_launch": 189097704704},
-    # k_apply_bnd: FETCH_SIZE 7,569,698.12 KiB * 2.0 + WRITE_SIZE 15,072,114.70 KiB * 1.0, averaged over 37
+    "dense-7b": {"src": "53d67aba3946e0d0", "bytes_per_launch": 189097660323},
+    # k_apply_bnd: FETCH_SIZE 7,569,690.44 KiB * 2.0 + WRITE_SIZE 15,072,217.06 KiB * 1.0, averaged over 37
     # dispatches (profiles/k_apply_llama3-70b_kernel_trace.md)
-    "llama3-70b": {"src": "98df89ac165834d2", "bytes_per_launch": 30936587209},
+    "llama3-70b": {"src": "53d67aba3946e0d0", "bytes_per_launch": 30936676290},
     # both buffers' launches of one step (the bf16-param / fp32-grad window and the fp32 norms):
-    # FETCH_SIZE 7,872,472.42 + 311.88 KiB * 2.0 + WRITE_SIZE 13,723,597.60 + 390.00 KiB * 1.0, averaged
+    # FETCH_SIZE 7,872,477.81 + 310.13 KiB * 2.0 + WRITE_SIZE 13,723,600.49 + 390.00 KiB * 1.0, averaged
     # over 37 dispatches each (profiles/k_apply_llama3-8b_kernel_trace.md)
-    "llama3-8b": {"src": "98df89ac165834d2", "bytes_per_launch": 30176825531},
+    "llama3-8b": {"src": "53d67aba3946e0d0", "bytes_per_launch": 30176835961},
 }
 
 
